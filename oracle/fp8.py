@@ -1,0 +1,174 @@
+"""fp8 (OCP e4m3) pieces of the oracle: codec, Hadamard rotation, quantisation.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources
+-------
+"FlashAttention-3 : une attention plus rapide ...", section "Fonctionnalites
+des GPU Hopper : WGMMA, TMA, FP8": fp8 doubles matrix throughput at a cost in
+precision.  Same page, section "Basse precision FP8 et incoherent processing":
+Q and K are multiplied by a random orthogonal matrix, a Hadamard transform with
+random signs applied per head in O(d log d), to spread outliers before
+quantisation.  Readings taken where the page is silent: the normalised
+Sylvester matrix H_d / sqrt(d); one seeded +-1 sign vector D shared by all
+heads; Q' = Q D H, K' = K D H, V not rotated; one fp32 scale per tile of 128
+tokens of one head (scale = amax / 448, 1 when the tile is all zero); codes are
+OCP e4m3 (no infinities, max finite 448) rounded to nearest-even with
+saturation at +-448.
+
+Everything here is float64 except the stored scale, which is rounded to
+float32 because that is what the quantised format carries.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+SCALE_TILE = 128
+
+
+def e4m3_value(code):
+    """Decode e4m3 codes (uint8 array-like) from the format definition.
+
+    bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa.
+    exponent 0: subnormal, value 2^-6 * m/8.  S.1111.111 is NaN; no infinities.
+    """
+    c = np.asarray(code, dtype=np.int64) & 0xFF
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+_POS_CODES = np.arange(0x7F, dtype=np.int64)          # 0x00..0x7E: all non-negative finite codes
+_POS_VALS = e4m3_value(_POS_CODES)                     # strictly increasing with the code
+
+
+def e4m3_code(x):
+    """Round float64 values to e4m3 codes: nearest, ties to even mantissa, saturating.
+
+    NaN -> 0x7F.  |x| >= 448 -> 0x7E (448) with the sign of x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, np.minimum(a, E4M3_MAX))
+    hi = np.clip(np.searchsorted(_POS_VALS, a, side="left"), 0, len(_POS_VALS) - 1)
+    lo = np.clip(hi - 1, 0, len(_POS_VALS) - 1)
+    d_hi = _POS_VALS[hi] - a
+    d_lo = a - _POS_VALS[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (_POS_CODES[lo] % 2 == 0))
+    code = np.where(pick_lo, _POS_CODES[lo], _POS_CODES[hi])
+    code = np.where(np.signbit(x), code | 0x80, code)
+    code = np.where(nan, 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def e4m3_round(x):
+    """Value of x after an e4m3 round trip (float64)."""
+    return e4m3_value(e4m3_code(x))
+
+
+def hadamard(d):
+    """Normalised Sylvester-Hadamard matrix: H_1 = [1], H_2n = [[H, H], [H, -H]], / sqrt(d)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(d)
+
+
+def rotate(x, signs):
+    """x D H over the last axis (D = diag(signs)), float64."""
+    x = np.asarray(x, dtype=np.float64)
+    s = np.asarray(signs, dtype=np.float64)
+    return (x * s) @ hadamard(x.shape[-1])
+
+
+def quantize_rows(x, tile=SCALE_TILE):
+    """Per-tile quantisation of x [B, H, N, d] along the token axis N.
+
+    Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/tile)]).
+    scale = float32(amax / 448) (1 for an all-zero tile); code = e4m3(x / scale).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, H, N, d = x.shape
+    nt = -(-N // tile)
+    scales = np.empty((B, H, nt), dtype=np.float32)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    for t in range(nt):
+        blk = x[:, :, t * tile:(t + 1) * tile, :]
+        amax = np.abs(blk).max(axis=(2, 3))
+        sc = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+        scales[:, :, t] = sc
+        codes[:, :, t * tile:(t + 1) * tile, :] = e4m3_code(blk / sc.astype(np.float64)[:, :, None, None])
+    return codes, scales
+
+
+def dequantize_rows(codes, scales, tile=SCALE_TILE):
+    """Inverse of ``quantize_rows``: value(code) * scale, float64."""
+    v = e4m3_value(codes)
+    N = v.shape[2]
+    rep = np.repeat(np.asarray(scales, dtype=np.float64), tile, axis=2)[:, :, :N]
+    return v * rep[..., None]
+
+
+def prepare(q, k, v, signs, tile=SCALE_TILE):
+    """The fp8 prepare step: rotate Q and K, then quantise Q, K, V per tile.
+
+    Returns dict with the rotated float64 inputs and the (codes, scales) triples.
+    """
+    qr = rotate(q, signs)
+    kr = rotate(k, signs)
+    vv = np.asarray(v, dtype=np.float64)
+    return {
+        "q_rot": qr, "k_rot": kr,
+        "q": quantize_rows(qr, tile), "k": quantize_rows(kr, tile), "v": quantize_rows(vv, tile),
+    }
+
+
+def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=8, rotate_qk=True,
+                       tile=SCALE_TILE, heads=None):
+    """fp8 emulation of the whole path, float64 arithmetic.
+
+    Q, K (rotated when ``rotate_qk``) and V are quantised per tile and
+    dequantised; scores are exact on the dequantised values; the online softmax
+    walks key blocks of ``block_n`` and rounds each block's probabilities
+    p = exp(s - m_running) to e4m3 after scaling by 2**p_shift (the sum l uses
+    the unrounded p).  No mask (the fp8 workload is non-causal).
+    Returns (O, LSE) of the selected heads, [n, N, d] and [n, N].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if rotate_qk:
+        q, k = rotate(q, signs), rotate(k, signs)
+    qd = dequantize_rows(*quantize_rows(q, tile), tile)
+    kd = dequantize_rows(*quantize_rows(k, tile), tile)
+    vd = dequantize_rows(*quantize_rows(v, tile), tile)
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    sel = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+    Nk = k.shape[2]
+    outs, lses = [], []
+    two = float(2 ** p_shift)
+    for b, h in sel:
+        g = h // G
+        m = np.full(N, -np.inf)
+        l = np.zeros(N)
+        acc = np.zeros((N, d))
+        for j0 in range(0, Nk, block_n):
+            s = scale * (qd[b, h] @ kd[b, g, j0:j0 + block_n].T)
+            m_new = np.maximum(m, s.max(axis=1))
+            alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+            p = np.exp(s - m_new[:, None])
+            l = alpha * l + p.sum(axis=1)
+            p8 = e4m3_round(p * two) / two
+            acc = alpha[:, None] * acc + p8 @ vd[b, g, j0:j0 + block_n]
+            m = m_new
+        outs.append(acc / l[:, None])
+        lses.append(m + np.log(l))
+    return np.stack(outs), np.stack(lses)
