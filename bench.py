@@ -1,0 +1,136 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+
+A step is one fused forward (``attn_fwd``) over the whole batch of the
+workload, inputs resident in HBM. The default workload is the causal prefill
+(B=4, H=32, N=4096, d=128, bf16). Throughput counts mask-adjusted FLOPs: 4 d
+per allowed (query, key) pair (QK^T and PV), nothing for the softmax.
+
+Prints ONE JSON line with the metric, the per-launch roofline of the kernel
+(HIP events on the launch stream over the timed region, against the MI355X
+dense matrix peak of the arithmetic type) and the CPU float64 oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+from tiled_attention_05_amd import _lib, flops
+from tiled_attention_05_amd import inputs as I
+
+METRIC = "attention fwd TFLOPS (mask-adjusted FLOPs) and % of MI355X MFMA peak"
+# MI355X dense matrix peaks (256 CUs x 2.4 GHz): bf16 4096 FLOP/clk/CU, fp8 twice that, fp32 1/16 of bf16
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+HOST_CORES = 16   # the host-CPU share of one GPU on the benchmark machines
+
+
+def mask_name(m):
+    parts = [n for b, n in ((1, "causal"), (2, "window"), (4, "doc")) if m & b]
+    return "+".join(parts) or "none"
+
+
+def run_cpu_baseline(w, x, budget_s=15.0):
+    """Oracle on whole heads of the same inputs until ~budget_s of wall time."""
+    from oracle import attention as A
+    threads = max(1, min(HOST_CORES, len(os.sched_getaffinity(0))))
+    heads_all = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    order = heads_all[::max(1, len(heads_all) // 64)] + heads_all
+    done, fl, t0 = [], 0, time.perf_counter()
+    docs = x["doc_ids"]
+    per_head = flops.attention_flops(1, 1, w.N, w.N, w.d, w.mask, w.window,
+                                     None if docs is None else docs[:1])
+    i = 0
+    while time.perf_counter() - t0 < budget_s and i < len(order):
+        batch = [hb for hb in order[i:i + threads] if hb not in done]
+        i += threads
+        if not batch:
+            continue
+        A.attention(x["q"], x["k"], x["v"], w.scale, w.mask, w.window, docs, w.softcap, x["slopes"],
+                    heads=batch, threads=threads)
+        for b, h in batch:
+            row = None if docs is None else docs[b:b + 1]
+            fl += flops.attention_flops(1, 1, w.N, w.N, w.d, w.mask, w.window, row)
+        done += batch
+    dt = time.perf_counter() - t0
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {len(heads_all)} (batch, head) pairs, all {w.N} query rows each, "
+                      f"float64 numpy, {dt:.1f} s wall",
+            "seconds": round(dt, 2), "flops_per_head": per_head}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by independent (batch, head) groups with no exchange)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()
+
+    w = I.WORKLOADS[args.workload]
+    x = I.inputs(w)
+    dev = {k: (None if v is None else v.to("cuda").contiguous()) for k, v in x.items()}
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.N, device="cuda", dtype=torch.float32)
+    fl = flops.attention_flops(w.B, w.Hq, w.N, w.N, w.d, w.mask, w.window, x["doc_ids"])
+
+    def step():
+        _lib.fwd(q, k, v, scale=w.scale, mask=w.mask, window=w.window, doc_ids=dev["doc_ids"],
+                 softcap=w.softcap, alibi_slopes=dev["slopes"], out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_kernel = ev0.elapsed_time(ev1) / args.steps
+    value = fl / (ms_step * 1e-3) / 1e12
+    achieved = fl / (ms_kernel * 1e-3) / 1e12
+    dt = {"f32": "f32", "bf16": "bf16", "fp8": "fp8"}[w.dtype]
+    peak = PEAK_TFLOPS[dt]
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "mask": mask_name(w.mask), "window": w.window, "softcap": w.softcap,
+                   "alibi": w.alibi, "flops_per_step": fl, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_ms": round(ms_kernel, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * attn.h -- C ABI of the fused attention forward for MI355X (gfx950).
+ *
+ * The operation (the plain definition the library reproduces, computed tile by
+ * tile so that no N x N score matrix ever reaches device memory):
+ *
+ *     O   = softmax( mods( scale * Q K^T ) under mask ) V
+ *     LSE = log( sum_j exp( mods( scale * q_i . k_j ) ) )      over allowed j
+ *
+ * Sources: "FlashAttention-3 : une attention plus rapide et plus precise grace
+ * a l'asynchronisme et a la basse precision" (fr.news.hada.io), section
+ * "Rappel du fonctionnement de FlashAttention" (blocks move from HBM to SRAM,
+ * attention is computed per block, tiling plus softmax rescaling is exact);
+ * "Les kernels d'attention rapide et la fusion d'operateurs accelerent les
+ * modeles d'IA", section "Attention de type FlashAttention et attention
+ * paginee" (the full score matrix is never stored); "FlexAttention de PyTorch
+ * avec FlashAttention-4 change la donne", opening section (score and mask
+ * modifiers: soft-capping, ALiBi, sliding window, document masking) and
+ * section "Limitations actuelles" (block sparsity; no silent fallback here).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees or retains them, and never synchronises the host.
+ * - Tensors are contiguous, row-major, BHSD: Q and O are [B][Hq][Nq][d], K and
+ *   V are [B][Hkv][Nk][d], LSE is [B][Hq][Nq] float32 (natural log).
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   All work is enqueued on it; every call is safe to capture into a HIP graph.
+ * - Return value: ATTN_OK or a negative attn_status. Arguments are validated
+ *   before any HIP call; an invalid call has no side effect. Faults during
+ *   kernel execution surface, as for any stream API, at the caller's next
+ *   synchronisation.
+ * - No call keeps mutable global state; calls are thread-safe.
+ */
+#ifndef TILED_ATTN_H
+#define TILED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = -1,   /* NULL required pointer, bad size, bad flag, non-finite scalar */
+    ATTN_ERR_UNSUPPORTED = -2,   /* a valid request this build does not implement (no fallback) */
+    ATTN_ERR_HIP = -3            /* a HIP runtime call or kernel launch failed */
+} attn_status;
+
+typedef enum {
+    ATTN_F32 = 0,        /* Q, K, V, O float32 */
+    ATTN_BF16 = 1,       /* Q, K, V, O bfloat16 */
+    ATTN_FP8_E4M3 = 2    /* Q, K, V are buffers written by attn_fp8_prepare; O is bfloat16 */
+} attn_dtype;
+
+/* mask_kind bit flags */
+enum {
+    ATTN_MASK_NONE = 0,
+    ATTN_MASK_CAUSAL = 1,   /* key j allowed for query i iff j <= i + (Nk - Nq)               */
+    ATTN_MASK_WINDOW = 2,   /* with CAUSAL only: also (i + Nk - Nq) - j < window (W keys)      */
+    ATTN_MASK_DOC = 4       /* doc_ids[b][i] == doc_ids[b][j]; needs Nq == Nk; with/without CAUSAL */
+};
+
+/*
+ * attn_fwd -- fused attention forward.
+ *
+ * q, k, v    : input tensors (layouts above); element type from `dtype`.
+ * o          : output [B][Hq][Nq][d]; float32 for ATTN_F32, bfloat16 otherwise.
+ * lse        : float32 [B][Hq][Nq] natural-log log-sum-exp of the modified
+ *              scores of each row, or NULL to skip it. A row with no allowed key
+ *              gets O = 0 and LSE = -inf.
+ * B, Hq, Hkv : batch, query heads, key/value heads; Hq % Hkv == 0 and query head
+ *              h reads key/value head h / (Hq / Hkv) (grouped-query attention).
+ * Nq, Nk     : query and key lengths, >= 1.
+ * d          : head dimension: 64 or 128 (128 only for ATTN_FP8_E4M3).
+ * scale      : finite multiplier of q . k (usually 1/sqrt(d)).
+ * mask_kind  : ATTN_MASK_* flags.  window: width W >= 1, read only with WINDOW.
+ * doc_ids    : device int32 [B][Nk], non-decreasing along each row (packed
+ *              documents); required iff ATTN_MASK_DOC. A decreasing sequence
+ *              is a precondition violation (attn_block_mask_build flags it).
+ * softcap    : 0 for none, else > 0: s <- softcap * tanh(s / softcap), applied
+ *              to s = scale * q . k before the ALiBi bias.
+ * alibi_slopes: device float32 [Hq] or NULL: s <- s - slope[h] * (i - j).
+ * dtype      : attn_dtype.
+ * Errors     : ATTN_ERR_INVALID_ARG for NULL q/k/v/o, dims < 1, Hq % Hkv != 0,
+ *              non-finite scale, softcap < 0 or non-finite, unknown mask bits,
+ *              WINDOW with window < 1, DOC without doc_ids, unknown dtype;
+ *              ATTN_ERR_UNSUPPORTED for d not in {64, 128}, WINDOW without
+ *              CAUSAL, DOC with Nq != Nk, fp8 with d != 128, Nq != Nk, a
+ *              mask, soft-cap or ALiBi; ATTN_ERR_HIP if the launch fails.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int mask_kind, int window, const int32_t* doc_ids,
+             float softcap, const float* alibi_slopes, int dtype, void* stream);
+
+/*
+ * fp8 incoherent-processing prepare step ("FlashAttention-3 : ...", section
+ * "Basse precision FP8 et incoherent processing": Q and K are multiplied by a
+ * Hadamard transform with random signs, per head, in O(d log d), to spread
+ * outliers before fp8 quantisation).
+ *
+ * Packed buffer format (one per tensor), for H heads and N tokens, with
+ * Np = N rounded up to a multiple of 128:
+ *   bytes [0, B*H*Np*d)        e4m3 (OCP, max 448) codes;
+ *                              Q and K: [B][H][Np][d] (rows rotated: x D H);
+ *                              V:       [B][H][d][Np] (transposed, not rotated);
+ *                              padding rows / columns hold 0.
+ *   then, at byte offset B*H*Np*d, float32 scales [B][H][Np/128]: one per
+ *   tile of 128 tokens of one head; value = scale * code (scale = tile
+ *   amax / 448, 1 for an all-zero tile); codes are rounded to nearest even
+ *   and saturate at +-448.
+ * attn_fp8_buffer_bytes gives the size of one such buffer (0 on bad sizes).
+ *
+ * q, k, v : device bfloat16 BHSD inputs, Q [B][Hq][N][d], K/V [B][Hkv][N][d].
+ * signs   : device int8 [d] of +-1 (the random diagonal D), shared by all heads.
+ * q8, k8, v8 : device buffers of attn_fp8_buffer_bytes(B, Hq|Hkv, N, d) bytes.
+ * d must be 128. Errors as for attn_fwd.
+ */
+size_t attn_fp8_buffer_bytes(int B, int H, int N, int d);
+int attn_fp8_prepare(const void* q, const void* k, const void* v,
+                     int B, int Hq, int Hkv, int N, int d, const int8_t* signs,
+                     void* q8, void* k8, void* v8, void* stream);
+
+/*
+ * Block mask builder ("FlexAttention de PyTorch ...", section "Limitations
+ * actuelles": block sparsity).  Classifies every (query tile, key tile) pair of
+ * a block_m x block_n tiling of the Nq x Nk score matrix of batch row b:
+ *   0 = empty (no allowed pair: skipped), 1 = partial (needs the element mask),
+ *   2 = full (every pair allowed: no mask code).
+ * Output buffer of attn_block_mask_bytes(...) bytes, laid out as
+ *   int8  kind[B][nQt][nKt]                     (nQt = ceil(Nq/block_m), nKt = ceil(Nk/block_n))
+ *   int32 counts[B][nQt][3]   at byte offset round_up(B*nQt*nKt, 16): empty, partial, full
+ *   int32 flags               after counts: bit 0 set iff some doc_ids row decreases
+ * block_m, block_n in [1, 4096]. Same mask semantics and errors as attn_fwd.
+ */
+size_t attn_block_mask_bytes(int B, int Nq, int Nk, int block_m, int block_n);
+int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window,
+                          const int32_t* doc_ids, int block_m, int block_n,
+                          void* out, void* stream);
+
+/* Static, human-readable text for an attn_status value (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TILED_ATTN_H */

@@ -135,7 +135,6 @@ def attention(q, k, v, scale, mask_kind=MASK_NONE, window=0, doc_ids=None, softc
     [n_heads_sel, n_rows] when ``heads``/``rows`` are given, else
     [B,Hq,Nq,d] and [B,Hq,Nq].
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
     if Hq % Hkv:
@@ -152,8 +151,9 @@ def attention(q, k, v, scale, mask_kind=MASK_NONE, window=0, doc_ids=None, softc
     def job(bh):
         b, h = bh
         g = h // G
-        return _head(q[b, h], k[b, g], v[b, g], rr, Nq, Nk, float(scale), mask_kind, window,
-                     None if docs is None else docs[b], float(softcap),
+        # upcast one head at a time (exact), so sampled checks stay small
+        return _head(_f64(q[b, h]), _f64(k[b, g]), _f64(v[b, g]), rr, Nq, Nk, float(scale), mask_kind,
+                     window, None if docs is None else docs[b], float(softcap),
                      None if slopes is None else float(slopes[h]), chunk)
 
     nthreads = threads or min(len(sel), os.cpu_count() or 1)

@@ -1,0 +1,191 @@
+"""GPU parity of the fused forward against the float64 oracle (through the C ABI).
+
+Small cases span several query / key tiles with ragged tails and run the whole
+oracle; the full workloads (in the launch configuration the benchmark times)
+are checked on sampled rows of sampled heads. Bars: max-abs 2e-2, mean-abs
+2e-3 on O, 1e-3 on LSE (the fp32 workload also meets 1e-4).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from tests.gpu_util import assert_close, oracle, run_fwd, to_dev
+from tiled_attention_05_amd import _lib
+from tiled_attention_05_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+C, W, D = I.MASK_CAUSAL, I.MASK_WINDOW, I.MASK_DOC
+
+
+def _case(w, seed=None, doc_range=None):
+    x = I.inputs(w, seed)
+    if doc_range is not None:
+        g = torch.Generator("cpu").manual_seed(77 + w.N)
+        rows = []
+        for _ in range(w.B):
+            lens = I.doc_lengths(w.N, g, *doc_range)
+            rows.append(torch.repeat_interleave(torch.arange(len(lens), dtype=torch.int32), torch.tensor(lens)))
+        x["doc_ids"] = torch.stack(rows)
+    return x
+
+
+def _check(w, x, label, **kw):
+    print(f"[case] {label} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} mask={w.mask}", flush=True)
+    o, lse = run_fwd(x, w.mask, w.window, w.softcap)
+    O, L = oracle(x, w.scale, w.mask, w.window, w.softcap)
+    return assert_close(o, lse, O, L, label=label, **kw)
+
+
+def test_tiny_dense_fp32_workload():
+    w = I.WORKLOADS[1]
+    x = I.inputs(w)
+    _check(w, x, "fp32 workload")
+    o, lse = run_fwd(x, w.mask)
+    O, L = oracle(x, w.scale, w.mask)
+    assert_close(o, lse, O, L, max_abs=1e-4, mean_abs=1e-5, lse_tol=1e-5, label="fp32 workload tight")
+
+
+SMALL = [
+    ("causal d128", I.WORKLOADS[2].shrink(B=2, Hq=3, Hkv=3, N=1000), None),
+    ("dense d128", I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=777, mask=0), None),
+    ("causal d64", I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=600, d=64), None),
+    ("dense d64", I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=333, d=64, mask=0), None),
+    ("gqa window", I.WORKLOADS[3].shrink(B=1, Hq=8, Hkv=2, N=1500, window=300), None),
+    ("gqa window tiny W", I.WORKLOADS[3].shrink(B=1, Hq=4, Hkv=2, N=700, window=1), None),
+    ("mqa causal", I.WORKLOADS[2].shrink(B=1, Hq=4, Hkv=1, N=520), None),
+    ("docs softcap alibi", I.WORKLOADS[4].shrink(B=1, Hq=4, Hkv=4, N=2500), (64, 1024)),
+    ("docs short", I.WORKLOADS[4].shrink(B=2, Hq=2, Hkv=2, N=900, softcap=0.0, alibi=False), (1, 40)),
+    ("docs non-causal", I.WORKLOADS[4].shrink(B=2, Hq=2, Hkv=2, N=700, mask=D, softcap=0.0, alibi=False),
+     (50, 300)),
+    ("softcap dense", I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=400, mask=0, softcap=5.0), None),
+    ("alibi causal", I.WORKLOADS[2].shrink(B=1, Hq=4, Hkv=4, N=400, alibi=True), None),
+    ("window softcap d64", I.WORKLOADS[3].shrink(B=1, Hq=2, Hkv=1, N=500, d=64, window=77, softcap=3.0), None),
+]
+
+
+@pytest.mark.parametrize("label,w,docs", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(label, w, docs):
+    _check(w, _case(w, doc_range=docs), label)
+
+
+@pytest.mark.parametrize("N", [1, 5, 63, 64, 65, 255, 257])
+@pytest.mark.parametrize("mask", [0, C])
+def test_short_sequences(N, mask):
+    w = I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=N, mask=mask)
+    _check(w, I.inputs(w, seed=N), f"N={N} mask={mask}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Nq,Nk", [(300, 1000), (1000, 300), (64, 65)])
+def test_rectangular_causal(dtype, Nq, Nk):
+    g = torch.Generator("cpu").manual_seed(Nq * 7 + Nk)
+    tq = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = {"q": torch.randn(1, 2, Nq, 64, generator=g).to(tq), "k": torch.randn(1, 2, Nk, 64, generator=g).to(tq),
+         "v": torch.randn(1, 2, Nk, 64, generator=g).to(tq)}
+    o, lse = run_fwd(x, C)
+    O, L = oracle(x, 0.125, C)
+    assert_close(o, lse, O, L, label=f"rect {dtype} {Nq}x{Nk}")
+    if Nq > Nk:
+        assert torch.all(o[:, :, :Nq - Nk].float() == 0)
+
+
+@pytest.mark.parametrize("mask,docs", [(C | W, None), (C | D, (20, 200)), (0, None)])
+def test_fp32_masks_and_mods(mask, docs):
+    w = I.WORKLOADS[1].shrink(B=1, Hq=2, Hkv=1, N=300, d=64, mask=mask, window=50, softcap=4.0, alibi=True)
+    x = _case(w, doc_range=docs)
+    _check(w, x, f"fp32 mask={mask}", max_abs=1e-4, mean_abs=1e-5, lse_tol=1e-4)
+
+
+def test_fp32_d128():
+    w = I.WORKLOADS[1].shrink(B=1, Hq=2, Hkv=2, N=200, d=128, mask=C)
+    _check(w, I.inputs(w), "fp32 d128", max_abs=1e-4, mean_abs=1e-5, lse_tol=1e-4)
+
+
+# ------------------------------------------------------------------ full workloads, sampled rows
+def _sample_rows(N, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, N // 2, N - 2, N - 1]
+    return np.unique(np.concatenate([[r for r in fixed if r < N], rng.integers(0, N, 19)]))
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_full_workload_sampled(k):
+    w = I.WORKLOADS[k]
+    print(f"[case] full workload {k} {w.name}", flush=True)
+    x = I.inputs(w)
+    o, lse = run_fwd(x, w.mask, w.window, w.softcap)
+    heads = [(b, h) for b in range(w.B) for h in sorted({0, w.Hq // 2, w.Hq - 1})]
+    rows = _sample_rows(w.N, k)
+    O, L = A.attention(x["q"], x["k"], x["v"], w.scale, w.mask, w.window, x["doc_ids"], w.softcap,
+                       x["slopes"], heads=heads, rows=rows)
+    og = torch.stack([o[b, h, rows] for b, h in heads])
+    lg = torch.stack([lse[b, h, rows] for b, h in heads])
+    assert_close(og, lg, O, L, label=f"workload {k} sampled")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+# ------------------------------------------------------------------ determinism, capture, canaries
+def test_bitwise_deterministic():
+    w = I.WORKLOADS[2].shrink(B=2, Hq=4, Hkv=4, N=1100)
+    x = I.inputs(w)
+    outs = [run_fwd(x, w.mask) for _ in range(4)]
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_graph_capture_replays_match_eager():
+    w = I.WORKLOADS[4].shrink(B=1, Hq=2, Hkv=2, N=1024)
+    x = _case(w, doc_range=(100, 400))
+    q, k, v, docs, sl = (to_dev(x[n]) for n in ("q", "k", "v", "doc_ids", "slopes"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device="cuda")
+    kw = dict(scale=w.scale, mask=w.mask, doc_ids=docs, softcap=w.softcap, alibi_slopes=sl, out=o, lse=lse)
+    o_ref, l_ref = _lib.fwd(q, k, v, **{**kw, "out": None, "lse": None})
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _lib.fwd(q, k, v, **kw)      # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _lib.fwd(q, k, v, **kw)
+    for _ in range(3):
+        o.fill_(7.0)
+        lse.fill_(7.0)
+        junk = torch.randn(1000, 1000, device="cuda") @ torch.randn(1000, 1000, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+        del junk
+
+
+def test_canaries_around_outputs_untouched():
+    w = I.WORKLOADS[2].shrink(B=1, Hq=3, Hkv=3, N=333)
+    x = I.inputs(w)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    n_o, n_l, pad = q.numel(), w.B * w.Hq * w.N, 4096
+    ob = torch.full((n_o + 2 * pad,), 3.0, dtype=torch.bfloat16, device="cuda")
+    lb = torch.full((n_l + 2 * pad,), 3.0, dtype=torch.float32, device="cuda")
+    o = ob[pad:pad + n_o].view(q.shape)
+    lse = lb[pad:pad + n_l].view(w.B, w.Hq, w.N)
+    _lib.fwd(q, k, v, mask=w.mask, out=o, lse=lse)
+    torch.cuda.synchronize()
+    for buf, n in ((ob, n_o), (lb, n_l)):
+        assert torch.all(buf[:pad].float() == 3.0) and torch.all(buf[pad + n:].float() == 3.0)
+    O, L = oracle(x, w.scale, w.mask)
+    assert_close(o, lse, O, L, label="canary case")
+
+
+def test_lse_optional():
+    w = I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=200)
+    x = I.inputs(w)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    o = _lib.fwd(q, k, v, mask=w.mask, with_lse=False)
+    o2, _ = _lib.fwd(q, k, v, mask=w.mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)

@@ -1,0 +1,199 @@
+"""ctypes binding of libattn.so (the C ABI declared in include/attn.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels. PyTorch provides device memory and the current stream. The
+low-level functions keep the C names and return the C status; the helpers
+``fwd``, ``fp8_prepare`` and ``block_mask`` allocate outputs with torch and
+raise ``AttnError`` on a non-zero status. There is no fallback: without the
+built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+F32, BF16, FP8_E4M3 = 0, 1, 2
+MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOC = 0, 1, 2, 4
+FP8_TILE = 128
+
+EXPORTS = ("attn_fwd", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_block_mask_bytes",
+           "attn_block_mask_build", "attn_status_string")
+
+_lib = None
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def load():
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(PATH):
+            raise RuntimeError(f"{PATH} is missing; build it with `python -m tiled_attention_05_amd.build`")
+        lib = ctypes.CDLL(PATH)
+        lib.attn_fwd.restype = _i
+        lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _f, _vp,
+                                 _i, _vp]
+        lib.attn_fp8_buffer_bytes.restype = _sz
+        lib.attn_fp8_buffer_bytes.argtypes = [_i, _i, _i, _i]
+        lib.attn_fp8_prepare.restype = _i
+        lib.attn_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]
+        lib.attn_block_mask_bytes.restype = _sz
+        lib.attn_block_mask_bytes.argtypes = [_i, _i, _i, _i, _i]
+        lib.attn_block_mask_build.restype = _i
+        lib.attn_block_mask_build.argtypes = [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [_i]
+        _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else (t if isinstance(t, int) else t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+# ------------------------------------------------------------------ C names
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(status).decode()
+
+
+status_string = attn_status_string
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, window, doc_ids, softcap,
+             alibi_slopes, dtype, stream=None) -> int:
+    return load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, scale,
+                           mask_kind, window, _ptr(doc_ids), softcap, _ptr(alibi_slopes), dtype,
+                           _stream(stream))
+
+
+def attn_fp8_buffer_bytes(B, H, N, d) -> int:
+    return load().attn_fp8_buffer_bytes(B, H, N, d)
+
+
+def attn_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8, stream=None) -> int:
+    return load().attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, _ptr(signs), _ptr(q8),
+                                   _ptr(k8), _ptr(v8), _stream(stream))
+
+
+def attn_block_mask_bytes(B, Nq, Nk, block_m, block_n) -> int:
+    return load().attn_block_mask_bytes(B, Nq, Nk, block_m, block_n)
+
+
+def attn_block_mask_build(B, Nq, Nk, mask_kind, window, doc_ids, block_m, block_n, out, stream=None) -> int:
+    return load().attn_block_mask_build(B, Nq, Nk, mask_kind, window, _ptr(doc_ids), block_m, block_n,
+                                        _ptr(out), _stream(stream))
+
+
+# ------------------------------------------------------------------ helpers
+def _need(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA/HIP tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def fwd(q, k, v, scale=None, mask=MASK_NONE, window=0, doc_ids=None, softcap=0.0, alibi_slopes=None,
+        with_lse=True, out=None, lse=None, stream=None):
+    """O (and LSE) of the fused forward for fp32 / bf16 BHSD tensors."""
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(q.dtype)
+    if dt is None:
+        raise ValueError("q must be float32 or bfloat16 (fp8: use fwd_fp8)")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, 4)
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    if doc_ids is not None:
+        _need(doc_ids, "doc_ids", torch.int32, 2)
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32, 1)
+    o = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty(B, Hq, Nq, device=q.device, dtype=torch.float32)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = attn_fwd(q, k, v, o, lse if with_lse else None, B, Hq, Hkv, Nq, Nk, d, sc, mask, window, doc_ids,
+                  softcap, alibi_slopes, dt, stream)
+    if st:
+        raise AttnError(st, "attn_fwd")
+    return (o, lse) if with_lse else o
+
+
+def fp8_prepare(q, k, v, signs, stream=None):
+    """Rotate Q, K (random-sign Hadamard) and quantise Q, K, V to packed e4m3 buffers."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(signs, "signs", torch.int8, 1)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    nq = attn_fp8_buffer_bytes(B, Hq, N, d)
+    nk = attn_fp8_buffer_bytes(B, Hkv, N, d)
+    q8 = torch.empty(nq, dtype=torch.uint8, device=q.device)
+    k8 = torch.empty(nk, dtype=torch.uint8, device=q.device)
+    v8 = torch.empty(nk, dtype=torch.uint8, device=q.device)
+    st = attn_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8, stream)
+    if st:
+        raise AttnError(st, "attn_fp8_prepare")
+    return q8, k8, v8
+
+
+def fwd_fp8(q8, k8, v8, B, Hq, Hkv, N, d, scale=None, with_lse=True, stream=None, out=None, lse=None):
+    """O (bf16) and LSE of the fp8 forward on buffers written by fp8_prepare."""
+    o = torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty(B, Hq, N, device=q8.device, dtype=torch.float32)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = attn_fwd(q8, k8, v8, o, lse if with_lse else None, B, Hq, Hkv, N, N, d, sc, MASK_NONE, 0, None,
+                  0.0, None, FP8_E4M3, stream)
+    if st:
+        raise AttnError(st, "attn_fwd(fp8)")
+    return (o, lse) if with_lse else o
+
+
+def fp8_unpack(buf, B, H, N, d, transposed=False):
+    """Views of a packed fp8 buffer: (codes uint8, scales float32)."""
+    npad = (N + FP8_TILE - 1) // FP8_TILE * FP8_TILE
+    n = B * H * npad * d
+    codes = buf[:n].view(B, H, d, npad) if transposed else buf[:n].view(B, H, npad, d)
+    scales = buf[n:n + B * H * (npad // FP8_TILE) * 4].view(torch.float32).view(B, H, npad // FP8_TILE)
+    return codes, scales
+
+
+def block_mask(B, Nq, Nk, mask, window=0, doc_ids=None, block_m=128, block_n=64, device="cuda",
+               stream=None):
+    """(kinds int8 [B, nQt, nKt], counts int32 [B, nQt, 3], flags int) of the block classification."""
+    nbytes = attn_block_mask_bytes(B, Nq, Nk, block_m, block_n)
+    if nbytes == 0:
+        raise AttnError(ERR_INVALID_ARG, "attn_block_mask_bytes")
+    out = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    st = attn_block_mask_build(B, Nq, Nk, mask, window, doc_ids, block_m, block_n, out, stream)
+    if st:
+        raise AttnError(st, "attn_block_mask_build")
+    nq, nk = -(-Nq // block_m), -(-Nk // block_n)
+    kb = (B * nq * nk + 15) // 16 * 16
+    kinds = out[:B * nq * nk].view(torch.int8).view(B, nq, nk)
+    counts = out[kb:kb + B * nq * 3 * 4].view(torch.int32).view(B, nq, 3)
+    flags = out[kb + B * nq * 12:kb + B * nq * 12 + 4].view(torch.int32)
+    return kinds, counts, flags

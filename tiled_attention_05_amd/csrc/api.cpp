@@ -1,0 +1,147 @@
+// C ABI of the fused attention forward: argument validation (before any HIP
+// call), kernel-instance dispatch and error mapping. The operations and their
+// sources are documented in include/attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/attn.h"
+#include "fwd_params.h"
+
+namespace attn {
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t st);
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, hipStream_t st);
+hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N,
+                              int d, const int8_t* signs, void* q8, void* k8, void* v8, hipStream_t st);
+hipError_t launch_block_mask(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int bm,
+                             int bn, void* out, hipStream_t st);
+}  // namespace attn
+
+namespace {
+
+constexpr int kKnownMask = ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW | ATTN_MASK_DOC;
+constexpr int kFp8Tile = 128;
+constexpr long long kMaxElems = (1LL << 40);
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("ATTN_LOG");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+// Mask / size checks shared by attn_fwd and the block-mask builder.
+int check_mask(int Nq, int Nk, int mask_kind, int window, const int32_t* doc_ids) {
+    if (mask_kind & ~kKnownMask) return ATTN_ERR_INVALID_ARG;
+    if ((mask_kind & ATTN_MASK_WINDOW) && window < 1) return ATTN_ERR_INVALID_ARG;
+    if ((mask_kind & ATTN_MASK_DOC) && doc_ids == nullptr) return ATTN_ERR_INVALID_ARG;
+    if ((mask_kind & ATTN_MASK_WINDOW) && !(mask_kind & ATTN_MASK_CAUSAL)) return ATTN_ERR_UNSUPPORTED;
+    if ((mask_kind & ATTN_MASK_DOC) && Nq != Nk) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    if (e == hipErrorNotSupported) return ATTN_ERR_UNSUPPORTED;
+    if (log_enabled()) std::fprintf(stderr, "[attn] HIP error: %s\n", hipGetErrorString(e));
+    return ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID_ARG: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_HIP: return "HIP runtime or launch error";
+        default: return "unknown status";
+    }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+             int Nq, int Nk, int d, float scale, int mask_kind, int window, const int32_t* doc_ids,
+             float softcap, const float* alibi_slopes, int dtype, void* stream) {
+    if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+    if (Hq % Hkv) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(softcap) || softcap < 0.f) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
+    if ((long long)B * Hq * Nq * d > kMaxElems || (long long)B * Hkv * Nk * d > kMaxElems)
+        return ATTN_ERR_INVALID_ARG;
+    if (const int r = check_mask(Nq, Nk, mask_kind, window, doc_ids)) return r;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (dtype == ATTN_FP8_E4M3 &&
+        (d != 128 || Nq != Nk || mask_kind != 0 || softcap != 0.f || alibi_slopes != nullptr))
+        return ATTN_ERR_UNSUPPORTED;
+
+    attn::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.doc = (mask_kind & ATTN_MASK_DOC) ? doc_ids : nullptr;
+    p.slopes = alibi_slopes;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+    p.group = Hq / Hkv;
+    p.mask = mask_kind;
+    p.window = (mask_kind & ATTN_MASK_WINDOW) ? window : 0;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.softcap = softcap;
+    p.npad = (Nk + kFp8Tile - 1) / kFp8Tile * kFp8Tile;
+    hipStream_t st = (hipStream_t)stream;
+    if (log_enabled())
+        std::fprintf(stderr, "[attn] fwd dtype=%d B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d mask=%d window=%d "
+                             "softcap=%g alibi=%d\n",
+                     dtype, B, Hq, Hkv, Nq, Nk, d, mask_kind, p.window, softcap, alibi_slopes != nullptr);
+    hipError_t e;
+    if (dtype == ATTN_BF16) e = attn::launch_fwd_bf16(p, d, st);
+    else if (dtype == ATTN_F32) e = attn::launch_fwd_f32(p, d, st);
+    else e = attn::launch_fwd_fp8(p, d, st);
+    return hip_status(e);
+}
+
+size_t attn_fp8_buffer_bytes(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    const size_t np = (size_t)(N + kFp8Tile - 1) / kFp8Tile * kFp8Tile;
+    const size_t data = (size_t)B * H * np * d;
+    return data + (size_t)B * H * (np / kFp8Tile) * sizeof(float);
+}
+
+int attn_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N, int d,
+                     const int8_t* signs, void* q8, void* k8, void* v8, void* stream) {
+    if (!q || !k || !v || !signs || !q8 || !k8 || !v8) return ATTN_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv) return ATTN_ERR_INVALID_ARG;
+    if ((long long)B * Hq * N * d > kMaxElems) return ATTN_ERR_INVALID_ARG;
+    if (d != 128) return ATTN_ERR_UNSUPPORTED;
+    return hip_status(attn::launch_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8,
+                                               (hipStream_t)stream));
+}
+
+size_t attn_block_mask_bytes(int B, int Nq, int Nk, int block_m, int block_n) {
+    if (B < 1 || Nq < 1 || Nk < 1 || block_m < 1 || block_n < 1 || block_m > 4096 || block_n > 4096)
+        return 0;
+    const size_t nq = (size_t)(Nq + block_m - 1) / block_m, nk = (size_t)(Nk + block_n - 1) / block_n;
+    const size_t kinds = ((size_t)B * nq * nk + 15) / 16 * 16;
+    return kinds + (size_t)B * nq * 3 * sizeof(int32_t) + sizeof(int32_t);
+}
+
+int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window, const int32_t* doc_ids,
+                          int block_m, int block_n, void* out, void* stream) {
+    if (!out) return ATTN_ERR_INVALID_ARG;
+    if (B < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_INVALID_ARG;
+    if (block_m < 1 || block_n < 1 || block_m > 4096 || block_n > 4096) return ATTN_ERR_INVALID_ARG;
+    if (const int r = check_mask(Nq, Nk, mask_kind, window, doc_ids)) return r;
+    return hip_status(attn::launch_block_mask(B, Nq, Nk, mask_kind,
+                                              (mask_kind & ATTN_MASK_WINDOW) ? window : 0,
+                                              (mask_kind & ATTN_MASK_DOC) ? doc_ids : nullptr, block_m,
+                                              block_n, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// Kernel argument block of the fused forward (host and device share it).
+#pragma once
+#include <stdint.h>
+
+namespace attn {
+
+enum : int { kMaskCausal = 1, kMaskWindow = 2, kMaskDoc = 4 };
+
+struct FwdParams {
+    const void* q;          // [B][Hq][Nq][d]   (fp8: packed buffer, rows padded to 128)
+    const void* k;          // [B][Hkv][Nk][d]  (fp8: packed buffer)
+    const void* v;          // [B][Hkv][Nk][d]  (fp8: packed, transposed [d][Np])
+    void* o;                // [B][Hq][Nq][d]
+    float* lse;             // [B][Hq][Nq] or nullptr
+    const int32_t* doc;     // [B][Nk] or nullptr
+    const float* slopes;    // [Hq] or nullptr
+    int B, Hq, Hkv, Nq, Nk;
+    int group;              // Hq / Hkv
+    int mask;               // kMask* flags
+    int window;
+    float scale;            // multiplier of q . k
+    float scale_log2;       // scale * log2(e)
+    float softcap;          // > 0 when soft-capping
+    int n_qt;               // query tiles per (b, h)
+    int n_bh;               // B * Hq
+    int npad;               // fp8: token count padded to the scale tile
+};
+
+}  // namespace attn
