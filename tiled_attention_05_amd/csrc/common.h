@@ -33,6 +33,22 @@ __device__ __forceinline__ void load_lds4(const void* src, ATTN_LDS void* lds_wa
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 4, 0, 0);
 }
 
+// Same copies issued from inline assembly: the compiler then does not know
+// that they write LDS, so it does not insert a wait for them before unrelated
+// LDS reads; the caller waits explicitly (wait_all_and_barrier) before reading
+// the destination. lds_wave_base is a wave-uniform LDS byte address (M0).
+__device__ __forceinline__ void dma16(const void* src, unsigned lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, unsigned lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ unsigned lds_addr(const ATTN_LDS void* p) {
+    return (unsigned)(uintptr_t)p;
+}
+
 // Wait until this wave's global loads (including global->LDS copies) have all
 // landed and its LDS reads have returned, then barrier the workgroup. The
 // empty asm statements keep the compiler from moving memory accesses across.
