@@ -42,8 +42,13 @@
 // for causal / window, from the tile's first / last document id for packed
 // documents.
 #include <climits>
+#include <type_traits>
 
 #include "fwd_common.h"
+
+#ifndef ATTN_PREFETCH
+#define ATTN_PREFETCH 2   // key/value tiles in flight ahead of the matrix work (1..3)
+#endif
 
 namespace attn {
 
@@ -57,7 +62,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     constexpr int DS = D / 16;   // GEMM0 k-steps
     constexpr int DT = D / 32;   // output d-subtiles
     constexpr bool MODS = SOFTCAP || ALIBI;
-    constexpr int NKB = 2, NVB = 3;   // key / value tile buffers
+    // Copies run PF tiles ahead of the matrix work; key tiles need PF + 1
+    // buffers, value tiles (read during two consecutive intervals) PF + 2.
+    constexpr int PF = ATTN_PREFETCH;
+    static_assert(PF >= 1 && PF <= 2, "prefetch distance 1 or 2");
+    constexpr int NKB = PF + 1, NVB = PF + 2;
+    using Copy = TileCopy<D, NW>;
+    constexpr int LOADS_PER_TILE = 2 * Copy::ROUNDS + (DOC ? 1 : 0);   // per wave
 
     __shared__ __attribute__((aligned(1024))) char tiles_lds[(NKB + NVB) * T::BYTES];
     __shared__ __attribute__((aligned(16))) int docs_lds[DOC ? NVB * NW * BN : 4];
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     }
 
     ATTN_LDS char* lds = (ATTN_LDS char*)tiles_lds;
-    auto kbuf = [&](int i) __attribute__((always_inline)) { return lds + (i & 1) * T::BYTES; };
+    auto kbuf = [&](int i) __attribute__((always_inline)) { return lds + (i % NKB) * T::BYTES; };
     auto vbuf = [&](int i) __attribute__((always_inline)) { return lds + (NKB + i % NVB) * T::BYTES; };
     auto dbuf = [&](int i) __attribute__((always_inline)) {
         return (ATTN_LDS int*)docs_lds + (i % NVB) * (NW * BN);
@@ -190,63 +201,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         return full;
     };
 
-    // softmax of one key tile: scores -> P (bf16), running max / sum; the
-    // output accumulator is rescaled only when the exponent reference moves.
     bf16x8 pf[2][2];
-    auto softmax = [&](bool full, int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
-        const int j0 = kt * BN;
-        const bool general = MODS || !full;
-        float mx;
-        if (!general) {
-            float a0 = fmaxf(sacc[0][0], sacc[0][1]), a1 = fmaxf(sacc[1][0], sacc[1][1]);
-#pragma unroll
-            for (int r = 2; r < 16; r += 2) {
-                a0 = fmaxf(a0, fmaxf(sacc[0][r], sacc[0][r + 1]));
-                a1 = fmaxf(a1, fmaxf(sacc[1][r], sacc[1][r + 1]));
-            }
-            mx = xhalf_max(fmaxf(a0, a1)) * c;
-        } else {
-            int dk[2][16];
-            if (DOC && !full) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const i32x4 dv = *(const ATTN_LDS i32x4*)(dl + wave * BN + 32 * kb + 8 * gq + 4 * hh);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) dk[kb][4 * gq + e] = dv[e];
-                    }
-            }
-            // allowed keys of this row within the tile: jl_lo <= jl <= jl_hi
-            const int jl_hi = min(Nk - 1 - j0, causal ? row + off - j0 : INT_MAX / 2);
-            const int jl_lo = windowed ? row + off - W + 1 - j0 : 0;
-            float a0 = -INFINITY, a1 = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
-                    float y;
-                    if (SOFTCAP) {
-                        // cap * tanh(x / cap) = cap - 2 cap / (exp(2 x / cap) + 1), in exp2 units
-                        const float e = fast_exp2(sacc[kb][r] * cap_in);
-                        y = cap_l2 - 2.f * cap_l2 * fast_rcp(e + 1.f);
-                    } else {
-                        y = sacc[kb][r] * c;
-                    }
-                    if (ALIBI) y -= slope_l2 * (float)(row - (j0 + jl));
-                    if (!full) {
-                        bool ok = jl <= jl_hi;
-                        if (windowed) ok &= jl >= jl_lo;
-                        if (DOC) ok &= dk[kb][r] == doc_i;
-                        y = ok ? y : -INFINITY;
-                    }
-                    sacc[kb][r] = y;
-                    if (kb == 0) a0 = fmaxf(a0, y); else a1 = fmaxf(a1, y);
-                }
-            }
-            mx = xhalf_max(fmaxf(a0, a1));
-        }
+    float rescale_by = 1.f;      // output factor of the last softmax (1 for most rows)
+    bool rescale_any = false;    // some row of the wave needs it
+    // Online-softmax update shared by both softmax variants: new reference max,
+    // rescale factor, then p = exp2(y - m) into bf16 P and the running sum. The
+    // reference only moves when the row max grew by more than 2^kLazyTau.
+    auto finish = [&](float mx, auto&& ys) __attribute__((always_inline)) {
         const float mold = m;
         const float mn = fmaxf(mold, mx);
         const bool upd = mold == -INFINITY || mn > mold + kLazyTau;
@@ -260,20 +221,82 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float x0 = general ? sacc[kb][r] - mu : __builtin_fmaf(sacc[kb][r], c, -mu);
-                const float x1 = general ? sacc[kb][r + 1] - mu : __builtin_fmaf(sacc[kb][r + 1], c, -mu);
-                const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
+                const float p0 = fast_exp2(ys(kb, r, mu)), p1 = fast_exp2(ys(kb, r + 1, mu));
                 if (r & 2) { ls2 += p0; ls3 += p1; } else { ls0 += p0; ls1 += p1; }
                 pf[kb][r >> 3][(r & 7)] = (__bf16)p0;
                 pf[kb][r >> 3][(r & 7) + 1] = (__bf16)p1;
             }
         l = l * alpha + ((ls0 + ls1) + (ls2 + ls3));
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float a = need ? alpha : 1.f;
-#pragma unroll
-            for (int t = 0; t < DT; ++t) o[t] *= a;
-        }
+        rescale_by = need ? alpha : 1.f;
+        rescale_any = __builtin_amdgcn_ballot_w64(need) != 0;
     };
+
+    // Full tile, no score modifier: the max is taken on raw q.k and the scale
+    // is folded into the exponent argument, one FMA per score.
+    auto softmax_plain = [&]() __attribute__((always_inline)) {
+        float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) {
+            a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
+            a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
+        }
+        a0 = max3(a0, sacc[0][15], a1);
+        const float mx = xhalf_max(fmaxf(a0, sacc[1][15])) * c;
+        finish(mx, [&](int kb, int r, float mu) __attribute__((always_inline)) {
+            return __builtin_fmaf(sacc[kb][r], c, -mu);
+        });
+    };
+
+    // Score modifiers and / or the element mask (partial tiles): the modified
+    // score in exp2 units replaces the raw one, masked entries become -inf.
+    auto softmax_general = [&](bool full, int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
+        const int j0 = kt * BN;
+        int dk[2][16];
+        if (DOC && !full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const i32x4 dv = *(const ATTN_LDS i32x4*)(dl + wave * BN + 32 * kb + 8 * gq + 4 * hh);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dk[kb][4 * gq + e] = dv[e];
+                }
+        }
+        // allowed keys of this row within the tile: jl_lo <= jl <= jl_hi
+        const int jl_hi = full ? BN : min(Nk - 1 - j0, causal ? row + off - j0 : INT_MAX / 2);
+        const int jl_lo = (windowed && !full) ? row + off - W + 1 - j0 : 0;
+        const bool mask_doc = DOC && !full;
+        float a0 = -INFINITY, a1 = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
+                float y;
+                if (SOFTCAP) {
+                    // cap * tanh(x / cap) = cap - 2 cap / (exp(2 x / cap) + 1), in exp2 units
+                    const float e = fast_exp2(sacc[kb][r] * cap_in);
+                    y = cap_l2 - 2.f * cap_l2 * fast_rcp(e + 1.f);
+                } else {
+                    y = sacc[kb][r] * c;
+                }
+                if (ALIBI) y -= slope_l2 * (float)(row - (j0 + jl));
+                bool ok = jl <= jl_hi && jl >= jl_lo;
+                if (DOC) ok &= !mask_doc || dk[kb][r] == doc_i;
+                y = ok ? y : -INFINITY;
+                sacc[kb][r] = y;
+                if (kb == 0) a0 = fmaxf(a0, y); else a1 = fmaxf(a1, y);
+            }
+        }
+        const float mx = xhalf_max(fmaxf(a0, a1));
+        finish(mx, [&](int kb, int r, float mu) __attribute__((always_inline)) { return sacc[kb][r] - mu; });
+    };
+
+    auto softmax = [&](bool full, int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
+        if (!MODS && full) softmax_plain();
+        else softmax_general(full, kt, dl);
+    };
+
 
     auto gemm1 = [&](const ATTN_LDS char* vl) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
@@ -303,38 +326,53 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     };
 
     auto in_w = [&](int kt) __attribute__((always_inline)) { return kt >= wt_begin && kt < wt_end; };
+    Copy copy;
+    copy.init(wave, lane);
     auto tile_k = [&](int i) __attribute__((always_inline)) {
-        issue_rows<D, NW, false>(K, (kt_begin + i) * BN, Nk, lds_addr(kbuf(i)), wave, lane);
+        copy.template issue<false>(K, (kt_begin + i) * BN, Nk, lds_addr(kbuf(i)), wave);
     };
     auto tile_v = [&](int i) __attribute__((always_inline)) {
-        issue_rows<D, NW, true>(V, (kt_begin + i) * BN, Nk, lds_addr(vbuf(i)), wave, lane);
+        copy.template issue<true>(V, (kt_begin + i) * BN, Nk, lds_addr(vbuf(i)), wave);
         if (DOC) issue_docs(docrow, (kt_begin + i) * BN, Nk, lds_addr(dbuf(i)), wave, lane);
     };
 
     // ---------------------------------------------------------------- ping-pong loop
     // Barrier i (i >= 1) is passed by group B at the top of body(i - 1) and by
-    // group A in the middle of body(i - 1); after it each wave issues its share
-    // of the copies of K(i + 1) and V(i + 1) (+ document ids), which land before
-    // barrier i + 1. Between barriers i and i + 1 the waves read K(i), V(i - 1)
-    // and V(i), never a buffer being refilled.
+    // group A in the middle of body(i - 1). Before it, each wave waits for its
+    // copies of tile i only (tile i + 1 may still be in flight when PF = 2);
+    // after it, it issues its share of tile i + PF. Between barriers i and i + 1
+    // the waves read K(i), V(i - 1) and V(i), never a buffer being refilled.
     auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
-        wait_all_and_barrier();
-        if (i + 1 < n_tiles) {
-            tile_k(i + 1);
-            tile_v(i + 1);
+        asm volatile("" ::: "memory");
+        if (PF >= 2 && i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
+        else __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (i + PF < n_tiles) {
+            tile_k(i + PF);
+            tile_v(i + PF);
         }
     };
     if (n_tiles > 0) {
-        tile_k(0);
-        tile_v(0);
+#pragma unroll
+        for (int i = 0; i < PF; ++i)
+            if (i < n_tiles) {
+                tile_k(i);
+                tile_v(i);
+            }
         barrier_and_copy(0);
         if (in_w(kt_begin)) gemm0(kbuf(0));
     }
+
     for (int it = 0; it < n_tiles; ++it) {
         const int kt = kt_begin + it;
         if (group_b) barrier_and_copy(it + 1);
         if (in_w(kt)) {
             softmax(is_full(kt, dbuf(it)), kt, dbuf(it));
+            if (__builtin_expect(rescale_any, 0)) {   // rare: the reference max moved
+#pragma unroll
+                for (int t = 0; t < DT; ++t) o[t] *= rescale_by;
+            }
             gemm1(vbuf(it));
         }
         if (!group_b) barrier_and_copy(it + 1);

@@ -45,6 +45,15 @@ __device__ __forceinline__ void dma4(const void* src, unsigned lds_wave_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
 }
+// Scalar-base forms: address = sbase (wave-uniform, SGPR pair) + voff (per lane).
+__device__ __forceinline__ void dma16s(const void* sbase, unsigned voff, unsigned lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_wave_base), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, unsigned voff, unsigned lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds_wave_base), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 __device__ __forceinline__ unsigned lds_addr(const ATTN_LDS void* p) {
     return (unsigned)(uintptr_t)p;
 }
@@ -80,6 +89,13 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
 // OCP e4m3 x e4m3 -> f32, 32x32x64 (block scales fixed at 2^0).
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// max(a, b, c) in one instruction (hardware max semantics).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -47,29 +47,54 @@ __device__ int wave_search(const int32_t* a, int n, int x, int lane) {
     return bal ? min(hi, lo + __builtin_ctzll(bal)) : hi;
 }
 
-// Copy one BN-row tile of K (or V) into LDS with its swizzle: LDS slot s of
-// the tile (16 bytes) receives logical chunk (s % CPR) ^ swz(row) of row s / CPR.
-// Rows past Nk read row Nk - 1 (finite data that the mask then ignores).
-template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void issue_rows(const __bf16* X, int kv0, int Nk, unsigned tile_lds, int wave,
-                                           int lane) {
+// Copy of one BN-row tile of K (or V) into LDS with its swizzle: LDS slot s
+// of the tile (16 bytes) receives logical chunk (s % CPR) ^ swz(row) of row
+// s / CPR. A wave moves 64 slots per instruction; the lane's byte offset
+// within the tile is fixed, the tile base moves in scalar registers.
+template <int D, int NW>
+struct TileCopy {
     using T = Tile<D>;
-    constexpr int ROUNDS = BN * T::CPR / (NW * 64);
+    static constexpr int ROUNDS = BN * T::CPR / (NW * 64);
+    static constexpr int ROWS_PER_ROUND = NW * 64 / T::CPR;
     static_assert(ROUNDS * NW * 64 == BN * T::CPR, "tile must split evenly over the waves");
-#pragma unroll
-    for (int rd = 0; rd < ROUNDS; ++rd) {
-        const int s = (rd * NW + wave) * 64 + lane;
-        const int row = s / T::CPR, pc = s % T::CPR;
-        const int grow = min(kv0 + row, Nk - 1);
-        const int sw = IS_V ? T::swz_v(row) : T::swz_k(row);
-        dma16(X + (size_t)grow * D + (pc ^ sw) * 8, tile_lds + (rd * NW + wave) * 1024);
+    static_assert(ROUNDS == 1 || ROWS_PER_ROUND % 16 == 0, "swizzle must repeat across rounds");
+    int r0;             // tile row of this lane in round 0
+    unsigned k_chunk;   // swizzled byte offset within the row, K layout
+    unsigned v_chunk;   // same, V layout
+
+    __device__ __forceinline__ void init(int wave, int lane) {
+        const int s = wave * 64 + lane;
+        r0 = s / T::CPR;
+        const int pc = s % T::CPR;
+        k_chunk = (pc ^ T::swz_k(r0)) * 16;
+        v_chunk = (pc ^ T::swz_v(r0)) * 16;
     }
-}
+
+    // Rows past Nk re-read row Nk - 1 (finite data the mask then ignores).
+    template <bool IS_V>
+    __device__ __forceinline__ void issue(const __bf16* X, int kv0, int Nk, unsigned tile_lds, int wave) const {
+        const char* base = (const char*)X + (size_t)kv0 * T::ROW_BYTES;
+        const unsigned chunk = IS_V ? v_chunk : k_chunk;
+        if (kv0 + BN <= Nk) {
+#pragma unroll
+            for (int rd = 0; rd < ROUNDS; ++rd)
+                dma16s(base + rd * ROWS_PER_ROUND * T::ROW_BYTES, r0 * T::ROW_BYTES + chunk,
+                       tile_lds + (rd * NW + wave) * 1024);
+        } else {
+#pragma unroll
+            for (int rd = 0; rd < ROUNDS; ++rd) {
+                const int row = min(rd * ROWS_PER_ROUND + r0, Nk - 1 - kv0);
+                dma16s(base, row * T::ROW_BYTES + chunk, tile_lds + (rd * NW + wave) * 1024);
+            }
+        }
+    }
+};
 
 // Document ids of one key tile: every wave keeps its own copy (64 x 4 bytes).
 __device__ __forceinline__ void issue_docs(const int32_t* docrow, int kv0, int Nk, unsigned docs_lds, int wave,
                                            int lane) {
-    dma4(docrow + min(kv0 + lane, Nk - 1), docs_lds + wave * BN * 4);
+    const int j = min(lane, Nk - 1 - kv0);
+    dma4s(docrow + kv0, j * 4, docs_lds + wave * BN * 4);
 }
 
 }  // namespace attn
