@@ -115,7 +115,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * attn_fp8_buffer_bytes gives the size of one such buffer (0 on bad sizes).
  *
  * q, k, v : device bfloat16 BHSD inputs, Q [B][Hq][N][d], K/V [B][Hkv][N][d].
- * signs   : device int8 [d] of +-1 (the random diagonal D), shared by all heads.
+ * signs   : device int8 [d] of +-1 (the random diagonal D), shared by all heads;
+ *           NULL quantises Q and K without the rotation (for comparisons).
  * q8, k8, v8 : device buffers of attn_fp8_buffer_bytes(B, Hq|Hkv, N, d) bytes.
  * d must be 128. Errors as for attn_fwd.
  */

@@ -130,15 +130,23 @@ def prepare(q, k, v, signs, tile=SCALE_TILE):
     }
 
 
-def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=8, rotate_qk=True,
-                       tile=SCALE_TILE, heads=None):
-    """fp8 emulation of the whole path, float64 arithmetic.
+def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=4, rotate_qk=True,
+                       tile=SCALE_TILE, heads=None, lazy_tau=None):
+    """fp8 emulation of the whole path, float64 arithmetic (no mask).
 
-    Q, K (rotated when ``rotate_qk``) and V are quantised per tile and
-    dequantised; scores are exact on the dequantised values; the online softmax
-    walks key blocks of ``block_n`` and rounds each block's probabilities
-    p = exp(s - m_running) to e4m3 after scaling by 2**p_shift (the sum l uses
-    the unrounded p).  No mask (the fp8 workload is non-causal).
+    Q, K (rotated when ``rotate_qk``) and V are quantised per tile of ``tile``
+    tokens; scores are exact on the dequantised Q, K. The online softmax walks
+    key blocks of ``block_n`` with the exact running max m; each block's
+    probabilities p = exp(s - m) are stored as e4m3(p * 2^p_shift * s_v / s_vmax)
+    (s_v: the V scale of the block's tile, s_vmax: the largest V scale of the
+    head) and multiply the V codes; the running sum uses the unrounded p; the
+    output is rescaled by s_vmax / 2^p_shift at the end.
+
+    ``lazy_tau`` (natural-log units) selects the other valid reference schedule:
+    the exponent reference is moved to the running max only when that max has
+    grown by more than lazy_tau (p then stays below e^lazy_tau); in exact
+    arithmetic both schedules give the same O and LSE, in fp8 they round P on
+    different grids.
     Returns (O, LSE) of the selected heads, [n, N, d] and [n, N].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -148,7 +156,8 @@ def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=8, rotate_qk=T
         q, k = rotate(q, signs), rotate(k, signs)
     qd = dequantize_rows(*quantize_rows(q, tile), tile)
     kd = dequantize_rows(*quantize_rows(k, tile), tile)
-    vd = dequantize_rows(*quantize_rows(v, tile), tile)
+    vc, vs = quantize_rows(v, tile)
+    v8 = e4m3_value(vc)
     B, Hq, N, d = q.shape
     G = Hq // k.shape[1]
     sel = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
@@ -157,18 +166,23 @@ def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=8, rotate_qk=T
     two = float(2 ** p_shift)
     for b, h in sel:
         g = h // G
+        svmax = float(vs[b, g].max())
         m = np.full(N, -np.inf)
         l = np.zeros(N)
         acc = np.zeros((N, d))
         for j0 in range(0, Nk, block_n):
-            s = scale * (qd[b, h] @ kd[b, g, j0:j0 + block_n].T)
+            cols = slice(j0, min(j0 + block_n, Nk))
+            s = scale * (qd[b, h] @ kd[b, g, cols].T)
             m_new = np.maximum(m, s.max(axis=1))
+            if lazy_tau is not None:
+                m_new = np.where(np.isfinite(m) & (m_new <= m + lazy_tau), m, m_new)
             alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
             p = np.exp(s - m_new[:, None])
             l = alpha * l + p.sum(axis=1)
-            p8 = e4m3_round(p * two) / two
-            acc = alpha[:, None] * acc + p8 @ vd[b, g, j0:j0 + block_n]
+            r = float(vs[b, g, j0 // tile]) / svmax
+            p8 = e4m3_round(p * two * r)
+            acc = alpha[:, None] * acc + p8 @ v8[b, g, cols]
             m = m_new
-        outs.append(acc / l[:, None])
+        outs.append(acc * (svmax / two) / l[:, None])
         lses.append(m + np.log(l))
     return np.stack(outs), np.stack(lses)

@@ -97,7 +97,7 @@ def test_fp8_prepare_validation(lib):
     f = lib.attn_fp8_prepare
     assert f(None, FAKE, FAKE, 1, 1, 1, 8, 128, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, 1, 3, 2, 8, 128, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, 1, 2, 2, 8, 128, None, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, 1, 2, 2, 8, 128, FAKE, None, FAKE, FAKE, None) == _lib.ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, 1, 2, 2, 8, 64, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_UNSUPPORTED
 
 

@@ -142,10 +142,12 @@ def fwd(q, k, v, scale=None, mask=MASK_NONE, window=0, doc_ids=None, softcap=0.0
 
 
 def fp8_prepare(q, k, v, signs, stream=None):
-    """Rotate Q, K (random-sign Hadamard) and quantise Q, K, V to packed e4m3 buffers."""
+    """Rotate Q, K (random-sign Hadamard; none if signs is None) and quantise Q, K, V
+    to packed e4m3 buffers."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, 4)
-    _need(signs, "signs", torch.int8, 1)
+    if signs is not None:
+        _need(signs, "signs", torch.int8, 1)
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     nq = attn_fp8_buffer_bytes(B, Hq, N, d)

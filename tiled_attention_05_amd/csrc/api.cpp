@@ -116,7 +116,7 @@ size_t attn_fp8_buffer_bytes(int B, int H, int N, int d) {
 
 int attn_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N, int d,
                      const int8_t* signs, void* q8, void* k8, void* v8, void* stream) {
-    if (!q || !k || !v || !signs || !q8 || !k8 || !v8) return ATTN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !q8 || !k8 || !v8) return ATTN_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv) return ATTN_ERR_INVALID_ARG;
     if ((long long)B * Hq * N * d > kMaxElems) return ATTN_ERR_INVALID_ARG;
     if (d != 128) return ATTN_ERR_UNSUPPORTED;

@@ -1,11 +1,391 @@
-// fp8 path: placeholder until the e4m3 kernels are in place.
-#include "common.h"
-#include "fwd_params.h"
+// fp8 (OCP e4m3) path: the incoherent-processing prepare step and the fused
+// forward on fp8 matrix cores.
+//
+// "FlashAttention-3 : une attention plus rapide ...", section "Basse precision
+// FP8 et incoherent processing": Q and K are multiplied by a Hadamard transform
+// with random signs, per head, in O(d log d), which spreads outlier channels
+// before quantisation; section "Fonctionnalites des GPU Hopper : WGMMA, TMA,
+// FP8": fp8 doubles matrix throughput; section "Chevauchement de GEMM et
+// softmax grace a l'asynchronisme": the exponential does not get faster in fp8,
+// so the softmax / matrix overlap matters even more.
+#include <climits>
+#include <type_traits>
+
+#include "fwd_common.h"
 
 namespace attn {
-hipError_t launch_fwd_fp8(const FwdParams&, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_fp8_prepare(const void*, const void*, const void*, int, int, int, int, int,
-                              const int8_t*, void*, void*, void*, hipStream_t) {
-    return hipErrorNotSupported;
+
+constexpr int kFp8Tile = 128;        // tokens per quantisation scale
+constexpr float kE4m3Max = 448.f;
+constexpr float kFp8PShift = 4.f;    // P is stored as e4m3(p * 2^4 * s_v / s_vmax), p <= 2^4
+
+// -----------------------------------------------------------------------------
+// Prepare: one workgroup per (tensor, batch, head, 128-token tile), one thread
+// per token. Q and K rows: x <- (x * signs) H / sqrt(d) by an in-register fast
+// Walsh-Hadamard transform (Sylvester order, 7 butterfly stages for d = 128).
+// Then the tile's amax gives scale = amax / 448 and the codes are the
+// round-to-nearest-even e4m3 values of x / scale (clamped to +-448 first, so
+// nothing saturates to NaN). V is not rotated and is written transposed,
+// [d][tokens], so the attention kernel reads contiguous keys per lane.
+__global__ __launch_bounds__(128) void fp8_prepare_kernel(const __bf16* __restrict__ q,
+                                                          const __bf16* __restrict__ k,
+                                                          const __bf16* __restrict__ v, int B, int Hq,
+                                                          int Hkv, int N, int Np, const int8_t* __restrict__ signs,
+                                                          uint8_t* __restrict__ q8, uint8_t* __restrict__ k8,
+                                                          uint8_t* __restrict__ v8) {
+    constexpr int D = 128;
+    __shared__ float red[2];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[D][kFp8Tile];
+    const int nt = Np / kFp8Tile;
+    const int nq = B * Hq * nt, nk = B * Hkv * nt;
+    int id = blockIdx.x;
+    int which, H;
+    const __bf16* src;
+    uint8_t* dst;
+    if (id < nq) { which = 0; src = q; dst = q8; H = Hq; }
+    else if (id < nq + nk) { which = 1; id -= nq; src = k; dst = k8; H = Hkv; }
+    else { which = 2; id -= nq + nk; src = v; dst = v8; H = Hkv; }
+    const int tile = id % nt, bh = id / nt;
+    const int t = threadIdx.x;
+    const int row = tile * kFp8Tile + t;
+
+    float x[D];
+    if (row < N) {
+        const bf16x8* s8 = (const bf16x8*)(src + ((size_t)bh * N + row) * D);
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const bf16x8 w = s8[c];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[8 * c + e] = (float)w[e];
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d) x[d] = 0.f;
+    }
+    if (which < 2 && signs != nullptr) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) x[d] = signs[d] < 0 ? -x[d] : x[d];
+#pragma unroll
+        for (int len = 1; len < D; len <<= 1)
+#pragma unroll
+            for (int i = 0; i < D; i += 2 * len)
+#pragma unroll
+                for (int j = i; j < i + len; ++j) {
+                    const float a = x[j], b2 = x[j + len];
+                    x[j] = a + b2;
+                    x[j + len] = a - b2;
+                }
+        const float r = 0.08838834764831845f;   // 1 / sqrt(128)
+#pragma unroll
+        for (int d = 0; d < D; ++d) x[d] *= r;
+    }
+
+    float am = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) am = fmaxf(am, fabsf(x[d]));
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
+    if ((t & 63) == 0) red[t >> 6] = am;
+    __syncthreads();
+    am = fmaxf(red[0], red[1]);
+    const float sc = am > 0.f ? am / kE4m3Max : 1.f;
+    const float inv = 1.f / sc;
+    float* scales = (float*)(dst + (size_t)B * H * Np * D);
+    if (t == 0) scales[(size_t)bh * nt + tile] = sc;
+
+    uint32_t w[D / 4];
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+        const float a0 = fminf(fmaxf(x[d] * inv, -kE4m3Max), kE4m3Max);
+        const float a1 = fminf(fmaxf(x[d + 1] * inv, -kE4m3Max), kE4m3Max);
+        const float a2 = fminf(fmaxf(x[d + 2] * inv, -kE4m3Max), kE4m3Max);
+        const float a3 = fminf(fmaxf(x[d + 3] * inv, -kE4m3Max), kE4m3Max);
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, pk, true);
+        w[d / 4] = (uint32_t)pk;
+    }
+    if (which < 2) {
+        uint4* o = (uint4*)(dst + ((size_t)bh * Np + row) * D);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d) vt[d][t] = (uint8_t)(w[d >> 2] >> (8 * (d & 3)));
+        __syncthreads();
+        // thread t stores d-row t of the transposed tile: 128 consecutive tokens
+        const uint4* src4 = (const uint4*)&vt[t][0];
+        uint4* o = (uint4*)(dst + ((size_t)bh * D + t) * Np + (size_t)tile * kFp8Tile);
+#pragma unroll
+        for (int c = 0; c < kFp8Tile / 16; ++c) o[c] = src4[c];
+    }
 }
+
+hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N, int d,
+                              const int8_t* signs, void* q8, void* k8, void* v8, hipStream_t st) {
+    if (d != 128) return hipErrorNotSupported;
+    const int Np = (N + kFp8Tile - 1) / kFp8Tile * kFp8Tile;
+    const int nt = Np / kFp8Tile;
+    const long long blocks = (long long)B * (Hq + 2 * Hkv) * nt;
+    if (blocks > INT_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fp8_prepare_kernel, dim3((unsigned)blocks), dim3(128), 0, st, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, B, Hq, Hkv, N, Np, signs, (uint8_t*)q8, (uint8_t*)k8,
+                       (uint8_t*)v8);
+    return hipGetLastError();
+}
+
+// -----------------------------------------------------------------------------
+// fp8 forward, d = 128, no mask. Same tiling and two-waves-per-SIMD ping-pong
+// as the bf16 kernel (see attn_fwd_bf16.hip), on 32x32x64 e4m3 matrix cores:
+//   GEMM0  S^T = K8 Q8^T   per 64-key tile: 2 key blocks x 2 k-steps of 64.
+//          The K rows of block kb are read in the order
+//              pi(m) = 32 ((m >> 2) & 1) + 16 kb + 4 (m >> 3) + (m & 3)
+//          so that accumulator register r of half-wave h holds key
+//          32 h + 16 kb + r: every lane then owns 32 consecutive keys.
+//   GEMM1  O^T = V8^T P8^T  one 64-key instruction per 32 output columns; the
+//          32 consecutive keys of a lane are exactly the B operand, and V^T
+//          rows give the A operand with contiguous keys.
+// Scales: S = s_q s_k (q8 . k8) -- folded into the per-tile score multiplier.
+// P is stored as e4m3(p 2^4 s_v(t) / s_vmax), the factor folded into the exp2
+// bias; the running sum uses the unscaled p; the epilogue multiplies by
+// s_vmax / 2^4. The exponent reference moves only when the row max grows by
+// more than 2^4, so p 2^4 s_v / s_vmax stays below 448.
+struct Fp8Tile {
+    static constexpr int KROW = 128;                 // bytes per key row (d = 128)
+    static constexpr int VROW = 64;                  // bytes per V^T row (64 keys)
+    static constexpr int KBYTES = BN * KROW;         // 8 KiB
+    static constexpr int VBYTES = 128 * VROW;        // 8 KiB
+    static __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 7; }
+    static __device__ __forceinline__ int swz_v(int r) { return (r >> 2) & 3; }
+};
+
+template <bool RAGGED>
+__global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
+    using T = Fp8Tile;
+    constexpr int NW = 8, BM = NW * 32, D = 128;
+    constexpr int PF = 2, NKB = PF + 1, NVB = PF + 2;
+    constexpr float kTau = kFp8PShift;   // lazy-rescale threshold (log2 units)
+    __shared__ __attribute__((aligned(1024))) char tiles_lds[NKB * T::KBYTES + NVB * T::VBYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool group_b = wave >= NW / 2;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int wid = blockIdx.x;
+    const int qt = p.n_qt - 1 - wid / p.n_bh;
+    const int bh = wid % p.n_bh;
+    const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.group;
+    const int N = p.Nk, Np = p.npad, ntile = Np / kFp8Tile;
+    const int q0 = qt * BM;
+    const size_t bhq = (size_t)b * p.Hq + h, bhk = (size_t)b * p.Hkv + g;
+    const uint8_t* Q8 = (const uint8_t*)p.q + bhq * Np * D;
+    const uint8_t* K8 = (const uint8_t*)p.k + bhk * Np * D;
+    const uint8_t* V8 = (const uint8_t*)p.v + bhk * D * Np;
+    const float* qsc = (const float*)((const uint8_t*)p.q + (size_t)p.B * p.Hq * Np * D) + bhq * ntile;
+    const float* ksc = (const float*)((const uint8_t*)p.k + (size_t)p.B * p.Hkv * Np * D) + bhk * ntile;
+    const float* vsc = (const float*)((const uint8_t*)p.v + (size_t)p.B * p.Hkv * Np * D) + bhk * ntile;
+
+    const int wq0 = q0 + wave * 32;
+    const bool wave_active = wq0 < N;
+    const int row = wq0 + l32;
+    const int n_tiles = (N + BN - 1) / BN;
+
+    // largest V scale of the head (wave reduction over its tiles)
+    float svmax = 0.f;
+    for (int i = lane; i < ntile; i += 64) svmax = fmaxf(svmax, vsc[i]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) svmax = fmaxf(svmax, __shfl_xor(svmax, s));
+    const float log2_svmax = __builtin_amdgcn_logf(svmax);
+    const float sq = qsc[min(wq0, Np - 1) / kFp8Tile];
+    const float c_q = sq * p.scale_log2;
+
+    // Q fragments: lane holds row l32, bytes 64 s + 32 hh .. + 31
+    i32x8 qf[2];
+    {
+        const uint8_t* qr = Q8 + (size_t)min(row, Np - 1) * D + 32 * hh;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) qf[s] = *(const i32x8*)(qr + 64 * s);
+    }
+
+    f32x16 o[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+
+    // K reads: block kb, lane row pi(l32) (+16 kb), 16-byte chunks 4 s + 2 hh + {0, 1}
+    const int krow = 32 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
+    // V^T reads: row 32 t + l32, 16-byte chunks 2 hh + {0, 1}
+    ATTN_LDS char* lds = (ATTN_LDS char*)tiles_lds;
+    auto kbuf = [&](int i) __attribute__((always_inline)) { return lds + (i % NKB) * T::KBYTES; };
+    auto vbuf = [&](int i) __attribute__((always_inline)) {
+        return lds + NKB * T::KBYTES + (i % NVB) * T::VBYTES;
+    };
+
+    // tile copies: one 16-byte slot per lane per tile, for K and for V^T
+    const int s_slot = wave * 64 + lane;                      // 0..511
+    const int ck_row = s_slot >> 3, ck_pc = s_slot & 7;
+    const unsigned ck_off = ck_row * T::KROW + ((ck_pc ^ T::swz_k(ck_row)) << 4);
+    const int cv_row = s_slot >> 2, cv_pc = s_slot & 3;
+    const unsigned cv_off = cv_row * Np + ((cv_pc ^ T::swz_v(cv_row)) << 4);
+    auto tile_k = [&](int i) __attribute__((always_inline)) {
+        dma16s(K8 + (size_t)i * BN * D, ck_off, lds_addr(kbuf(i)) + wave * 1024);
+    };
+    auto tile_v = [&](int i) __attribute__((always_inline)) {
+        dma16s(V8 + (size_t)i * BN, cv_off, lds_addr(vbuf(i)) + wave * 1024);
+    };
+
+    f32x16 sacc[2];
+    auto gemm0 = [&](const ATTN_LDS char* kl) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int r = krow + 16 * kb;
+            const ATTN_LDS char* rb = kl + r * T::KROW;
+            const int sw = T::swz_k(r);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int c0 = 4 * s + 2 * hh;
+                const i32x4 lo = *(const ATTN_LDS i32x4*)(rb + ((c0 ^ sw) << 4));
+                const i32x4 hi = *(const ATTN_LDS i32x4*)(rb + (((c0 + 1) ^ sw) << 4));
+                const i32x8 kf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                sacc[kb] = mfma_fp8(kf, qf[s], s == 0 ? f32x16{} : sacc[kb]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    i32x8 pf;
+    float rescale_by = 1.f;
+    bool rescale_any = false;
+    auto softmax = [&](int it) __attribute__((always_inline)) {
+        const int tsc = (it * BN) / kFp8Tile;
+        const float c = c_q * ksc[tsc];                          // score multiplier, exp2 units
+        const float bias = kFp8PShift + __builtin_amdgcn_logf(vsc[tsc]) - log2_svmax;
+        const int jl_hi = RAGGED ? N - 1 - it * BN : BN;         // last valid key in the tile
+        float mx;
+        if (!RAGGED || jl_hi >= BN - 1) {
+            float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
+#pragma unroll
+            for (int r = 3; r < 15; r += 2) {
+                a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
+                a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
+            }
+            mx = xhalf_max(max3(a0, sacc[0][15], fmaxf(a1, sacc[1][15]))) * c;
+        } else {
+            float a = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jl = 32 * hh + 16 * kb + r;
+                    sacc[kb][r] = jl <= jl_hi ? sacc[kb][r] : -INFINITY;
+                    a = fmaxf(a, sacc[kb][r]);
+                }
+            mx = xhalf_max(a) * c;
+        }
+        const float mold = m;
+        const float mn = fmaxf(mold, mx);
+        const bool upd = mold == -INFINITY || mn > mold + kTau;
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = upd ? fast_exp2(mold - mref) : 1.f;
+        const bool need = upd && mold != -INFINITY;
+        m = upd ? mn : mold;
+        const float mb = (m == -INFINITY ? 0.f : m) - bias;
+        float ls0 = 0.f, ls1 = 0.f, ls2 = 0.f, ls3 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -mb));
+                const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r + 1], c, -mb));
+                const float p2 = fast_exp2(__builtin_fmaf(sacc[kb][r + 2], c, -mb));
+                const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][r + 3], c, -mb));
+                ls0 += p0; ls1 += p1; ls2 += p2; ls3 += p3;
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                pf[4 * kb + (r >> 2)] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, pk, true);
+            }
+        l = l * alpha + ((ls0 + ls1) + (ls2 + ls3)) * fast_exp2(-bias);
+        rescale_by = need ? alpha : 1.f;
+        rescale_any = __builtin_amdgcn_ballot_w64(need) != 0;
+    };
+
+    auto gemm1 = [&](const ATTN_LDS char* vl) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int r = 32 * t + l32;
+            const ATTN_LDS char* rb = vl + r * T::VROW;
+            const int sw = T::swz_v(r);
+            const i32x4 lo = *(const ATTN_LDS i32x4*)(rb + (((2 * hh) ^ sw) << 4));
+            const i32x4 hi = *(const ATTN_LDS i32x4*)(rb + (((2 * hh + 1) ^ sw) << 4));
+            const i32x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[t] = mfma_fp8(vf, pf, o[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
+        else __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (i + PF < n_tiles) {
+            tile_k(i + PF);
+            tile_v(i + PF);
+        }
+    };
+
+    if (n_tiles > 0) {
+        tile_k(0);
+        tile_v(0);
+        if (n_tiles > 1) {
+            tile_k(1);
+            tile_v(1);
+        }
+        barrier_and_copy(0);
+        if (wave_active) gemm0(kbuf(0));
+    }
+    for (int it = 0; it < n_tiles; ++it) {
+        if (group_b) barrier_and_copy(it + 1);
+        if (wave_active) {
+            softmax(it);
+            if (__builtin_expect(rescale_any, 0)) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o[t] *= rescale_by;
+            }
+            gemm1(vbuf(it));
+        }
+        if (!group_b) barrier_and_copy(it + 1);
+        if (wave_active && it + 1 < n_tiles) gemm0(kbuf(it + 1));
+    }
+
+    if (!wave_active) return;
+    const float lt = xhalf_sum(l);
+    const float inv = lt > 0.f ? svmax / (exp2f(kFp8PShift) * lt) : 0.f;
+    if (row < N) {
+        __bf16* orow = (__bf16*)p.o + (bhq * N + row) * D + 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                bf16x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[t][4 * gq + e] * inv);
+                *(bf16x4*)(orow + 32 * t + 8 * gq) = w;
+            }
+        if (p.lse && hh == 0)
+            p.lse[bhq * N + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    }
+}
+
+hipError_t launch_fwd_fp8(const FwdParams& p0, int d, hipStream_t st) {
+    if (d != 128) return hipErrorNotSupported;
+    FwdParams p = p0;
+    p.n_qt = (p.Nq + 255) / 256;
+    p.n_bh = p.B * p.Hq;
+    if (p.Nk % BN) hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3(p.n_qt * p.n_bh), dim3(512), 0, st, p);
+    else hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3(p.n_qt * p.n_bh), dim3(512), 0, st, p);
+    return hipGetLastError();
+}
+
 }  // namespace attn
