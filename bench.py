@@ -16,9 +16,11 @@ a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -31,6 +33,46 @@ METRIC = "attention fwd TFLOPS (mask-adjusted FLOPs) and % of MI355X MFMA peak"
 # MI355X dense matrix peaks (256 CUs x 2.4 GHz): bf16 4096 FLOP/clk/CU, fp8 twice that, fp32 1/16 of bf16
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 HOST_CORES = 16   # the host-CPU share of one GPU on the benchmark machines
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "tiled_attention_05_amd", "csrc")
+# kernel sources whose hash keys the measured HBM traffic of a profile summary
+KERNEL_SOURCES = {"bf16": ["attn_fwd_bf16.hip", "fwd_common.h", "common.h", "fwd_params.h"],
+                  "fp8": ["fp8.hip", "fwd_common.h", "common.h", "fwd_params.h"],
+                  "f32": ["attn_fwd_f32.hip", "fwd_common.h", "common.h", "fwd_params.h"]}
+PROFILE_SUMMARY = {2: "profiles/fwd_bf16_causal_prefill_b4_h32_n4096_d128.md",
+                   5: "profiles/fwd_fp8_dense_b4_h16_n8192_d128.md"}
+
+
+def sources_hash(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, PROFILE_SUMMARY.get(workload, "-"))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    hm = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
+    tm = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not hm or not tm or hm.group(1) != sources_hash(kind):
+        return None
+    return int(tm.group(1))
+
+
+def calibrate_copy(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}))
 
 
 def mask_name(m):
@@ -72,7 +114,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -83,19 +126,33 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     _lib.load()
 
     w = I.WORKLOADS[args.workload]
     x = I.inputs(w)
     dev = {k: (None if v is None else v.to("cuda").contiguous()) for k, v in x.items()}
     q, k, v = dev["q"], dev["k"], dev["v"]
-    o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.N, device="cuda", dtype=torch.float32)
     fl = flops.attention_flops(w.B, w.Hq, w.N, w.N, w.d, w.mask, w.window, x["doc_ids"])
+    extra = {}
+    if w.dtype == "fp8":
+        q8, k8, v8 = _lib.fp8_prepare(q, k, v, dev["signs"])
+        o = torch.empty(w.B, w.Hq, w.N, w.d, dtype=torch.bfloat16, device="cuda")
 
-    def step():
-        _lib.fwd(q, k, v, scale=w.scale, mask=w.mask, window=w.window, doc_ids=dev["doc_ids"],
-                 softcap=w.softcap, alibi_slopes=dev["slopes"], out=o, lse=lse)
+        def step():
+            _lib.fwd_fp8(q8, k8, v8, w.B, w.Hq, w.Hkv, w.N, w.d, scale=w.scale, out=o, lse=lse)
+
+        def prep():
+            _lib.fp8_prepare(q, k, v, dev["signs"])
+    else:
+        o = torch.empty_like(q)
+
+        def step():
+            _lib.fwd(q, k, v, scale=w.scale, mask=w.mask, window=w.window, doc_ids=dev["doc_ids"],
+                     softcap=w.softcap, alibi_slopes=dev["slopes"], out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -115,6 +172,21 @@ def main():
     achieved = fl / (ms_kernel * 1e-3) / 1e12
     dt = {"f32": "f32", "bf16": "bf16", "fp8": "fp8"}[w.dtype]
     peak = PEAK_TFLOPS[dt]
+    if w.dtype == "fp8":
+        # the prepare step (Hadamard + quantisation) is HBM-bound: timed on its own
+        for _ in range(2):
+            prep()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            prep()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_prep = e0.elapsed_time(e1) / 10
+        prep_bytes = 2 * (q.numel() + k.numel() + v.numel()) + q8.numel() + k8.numel() + v8.numel()
+        extra = {"prepare_ms": round(ms_prep, 4), "prepare_GBps": round(prep_bytes / ms_prep / 1e6, 1),
+                 "end_to_end_tflops": round(fl / ((ms_prep + ms_kernel) * 1e-3) / 1e12, 2)}
+    traffic = measured_traffic(args.workload, dt)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -124,9 +196,11 @@ def main():
                    "mask": mask_name(w.mask), "window": w.window, "softcap": w.softcap,
                    "alibi": w.alibi, "flops_per_step": fl, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_ms": round(ms_kernel, 4)},
     }
+    if extra:
+        out["fp8_prepare"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
