@@ -137,6 +137,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int s = 0; s < DS; ++s) qf[s] = *(const bf16x8*)(qr + 16 * s);
     }
+    // Retire every compiler-visible global load here. The tile copies below
+    // are inline asm the compiler does not count, so a load still pending at
+    // the loop would get in-loop vmcnt waits that also drain the prefetches.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     f32x16 o[DT];
 #pragma unroll

@@ -19,6 +19,10 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define ATTN_LDS __attribute__((address_space(3)))
 
+// Read-only global memory reached through the scalar cache: a wave-uniform
+// load from it is an s_load (counted by lgkmcnt, not vmcnt).
+#define ATTN_CONST __attribute__((address_space(4)))
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -71,7 +75,9 @@ __device__ __forceinline__ void wait_all_and_barrier() {
 // Value held by lane l ^ 32 combined with this lane's: op(x[l], x[l ^ 32]).
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return m;
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -205,6 +205,13 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) qf[s] = *(const i32x8*)(qr + 64 * s);
     }
+    // Retire every compiler-visible global load before the loop: the tile
+    // copies are inline asm the compiler does not count, so a pending load
+    // would get in-loop vmcnt waits that also drain the prefetches.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // per-tile scales, read in the loop through the scalar cache
+    const ATTN_CONST float* ksc_s = (const ATTN_CONST float*)ksc;
+    const ATTN_CONST float* vsc_s = (const ATTN_CONST float*)vsc;
 
     f32x16 o[4];
 #pragma unroll
@@ -258,8 +265,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     bool rescale_any = false;
     auto softmax = [&](int it) __attribute__((always_inline)) {
         const int tsc = (it * BN) / kFp8Tile;
-        const float c = c_q * ksc[tsc];                          // score multiplier, exp2 units
-        const float bias = kFp8PShift + __builtin_amdgcn_logf(vsc[tsc]) - log2_svmax;
+        const float c = c_q * ksc_s[tsc];                        // score multiplier, exp2 units
+        const float bias = kFp8PShift + __builtin_amdgcn_logf(vsc_s[tsc]) - log2_svmax;
         const int jl_hi = RAGGED ? N - 1 - it * BN : BN;         // last valid key in the tile
         float mx;
         if (!RAGGED || jl_hi >= BN - 1) {
