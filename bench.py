@@ -32,6 +32,7 @@ from tiled_attention_05_amd import inputs as I
 METRIC = "attention fwd TFLOPS (mask-adjusted FLOPs) and % of MI355X MFMA peak"
 # MI355X dense matrix peaks (256 CUs x 2.4 GHz): bf16 4096 FLOP/clk/CU, fp8 twice that, fp32 1/16 of bf16
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+PEAK_MHZ = 2400.0   # the clock the published peaks assume
 HOST_CORES = 16   # the host-CPU share of one GPU on the benchmark machines
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tiled_attention_05_amd", "csrc")
@@ -51,18 +52,20 @@ def sources_hash(kind):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kind):
-    """HBM bytes per launch from the committed counter summary, if it was taken on
-    the current kernel sources (else None)."""
+def measured_profile(workload, kind):
+    """HBM bytes per launch and the graphics clock (MHz) from the committed
+    counter summary of this workload, if it was taken on the current kernel
+    sources (else None for each)."""
     path = os.path.join(ROOT, PROFILE_SUMMARY.get(workload, "-"))
     if not os.path.exists(path):
-        return None
+        return None, None
     text = open(path).read()
     hm = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
+    if not hm or hm.group(1) != sources_hash(kind):
+        return None, None
     tm = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not hm or not tm or hm.group(1) != sources_hash(kind):
-        return None
-    return int(tm.group(1))
+    cm = re.search(r"sclk_mhz:\s*([0-9.]+)", text)
+    return (int(tm.group(1)) if tm else None), (float(cm.group(1)) if cm else None)
 
 
 def calibrate_copy(nbytes=1 << 30, reps=3):
@@ -106,7 +109,9 @@ def run_cpu_baseline(w, x, budget_s=15.0):
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(done)} of {len(heads_all)} (batch, head) pairs, all {w.N} query rows each, "
                       f"float64 numpy, {dt:.1f} s wall",
-            "seconds": round(dt, 2), "flops_per_head": per_head}
+            "seconds": round(dt, 2), "flops_per_head": per_head,
+            "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                     "pool_threads": threads, "blas_threads_per_job": 1}}
 
 
 def main():
@@ -157,17 +162,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events on the launch stream around every launch of the timed region
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    ms_kernel = ev0.elapsed_time(ev1) / args.steps
+    ms_kernel = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     value = fl / (ms_step * 1e-3) / 1e12
     achieved = fl / (ms_kernel * 1e-3) / 1e12
     dt = {"f32": "f32", "bf16": "bf16", "fp8": "fp8"}[w.dtype]
@@ -186,7 +193,7 @@ def main():
         prep_bytes = 2 * (q.numel() + k.numel() + v.numel()) + q8.numel() + k8.numel() + v8.numel()
         extra = {"prepare_ms": round(ms_prep, 4), "prepare_GBps": round(prep_bytes / ms_prep / 1e6, 1),
                  "end_to_end_tflops": round(fl / ((ms_prep + ms_kernel) * 1e-3) / 1e12, 2)}
-    traffic = measured_traffic(args.workload, dt)
+    traffic, sclk = measured_profile(args.workload, dt)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -197,7 +204,14 @@ def main():
                    "alibi": w.alibi, "flops_per_step": fl, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel_ms": round(ms_kernel, 4)},
+                     "kernel_ms": round(ms_kernel, 4),
+                     "kernel_ms_median": round(per_launch[len(per_launch) // 2], 4),
+                     "kernel_ms_min": round(per_launch[0], 4),
+                     # the same peak scaled to the graphics clock the counter run of this
+                     # kernel measured (busy cycles / kernel time), when it is on record
+                     "sclk_mhz": sclk,
+                     "peak_at_sclk": None if sclk is None else round(peak * sclk / PEAK_MHZ, 1),
+                     "frac_at_sclk": None if sclk is None else round(achieved / (peak * sclk / PEAK_MHZ), 4)},
     }
     if extra:
         out["fp8_prepare"] = extra

@@ -36,6 +36,15 @@
 // the exponent reference is only moved when the row max has grown by more than
 // 2^8 ("lazy" rescale): the output accumulator is then rescaled rarely, and the
 // result is unchanged because O / l and the LSE use the same reference.
+// Masked tiles and score modifiers first rewrite the scores in place (exp2
+// units, -inf where not allowed); the softmax code is then the same.
+//
+// Register files: the matrix instructions are issued as inline assembly with
+// the output accumulator and the Q fragments in AGPRs (only the matrix core
+// reads them) and the scores / probabilities in VGPRs, so no copies between
+// the two files appear in the loop. Each wave runs its own loops around its
+// key range (the same number of barriers as every other wave), so the
+// steady-state body has no per-tile branches around the matrix work.
 //
 // Tiles are classified per wave as empty (outside the wave's contiguous key
 // range, skipped), partial (element mask) or full (no mask code): closed form
@@ -52,7 +61,8 @@
 
 namespace attn {
 
-constexpr float kLazyTau = 8.f;   // log2 units: rescale O only when the max grows by > 2^8
+constexpr float kLazyTau = 8.f;     // log2 units: rescale O only when the max grows by > 2^8
+constexpr float kNoMax = -1e30f;    // initial reference: finite, below any score
 
 template <int D, bool SOFTCAP, bool ALIBI, bool DOC>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
@@ -145,11 +155,18 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     f32x16 o[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    float m = kNoMax, l = 0.f;
+    // Matrix operands written by vector code: set here, pinned in their
+    // register files and followed by wait states, so none of these writes
+    // lands right before the first matrix instruction that reads it.
+#pragma unroll
+    for (int s = 0; s < DS; ++s) pin_a(qf[s]);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) pin_a(o[t]);
+    mfma_guard();
 
     // ---- lane-constant LDS offsets. With both swizzles, the offset of K-read
-    // step s is koff0 ^ (32 s) and of V d-subtile t is voff0 ^ (64 t): one base
-    // register each.
+    // step s is koff0 ^ (32 s) and of V d-subtile t is voff0 ^ (64 t).
     // K reads: row 32 kb + l32, logical chunk 2 s + hh.
     const int koff0 = l32 * T::ROW_BYTES + ((hh ^ T::swz_k(l32)) * 16);
     // V transposed reads: in each 16-lane group lane L addresses row R0 + L/4
@@ -161,6 +178,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         const int col = 16 * cg + 4 * (L & 3);
         voff0 = r * T::ROW_BYTES + ((((col * 2) >> 4) ^ T::swz_v(r)) << 4) + ((col * 2) & 15);
     }
+    int kofs[DS], vofs[DT];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kofs[s] = koff0 ^ (32 * s);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) vofs[t] = voff0 ^ (64 * t);
 
     ATTN_LDS char* lds = (ATTN_LDS char*)tiles_lds;
     auto kbuf = [&](int i) __attribute__((always_inline)) { return lds + (i % NKB) * T::BYTES; };
@@ -168,28 +190,72 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     auto dbuf = [&](int i) __attribute__((always_inline)) {
         return (ATTN_LDS int*)docs_lds + (i % NVB) * (NW * BN);
     };
+    // Per-lane fragment addresses of one tile: the tile base is added once
+    // and pinned there; the kb / u / row-half parts are immediate offsets.
+    auto tile_addr = [&](const ATTN_LDS char* base, const int* ofs, int* a, int n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            a[i] = (int)lds_addr(base) + ofs[i];
+            pin(a[i]);
+        }
+    };
+    auto at = [](int addr, int imm) __attribute__((always_inline)) {
+        return (const ATTN_LDS char*)(uintptr_t)addr + imm;
+    };
 
     // ---------------------------------------------------------------- stages
-    f32x16 sacc[2];
-    // Matrix phases keep at most two fragments in flight: the instruction
-    // groups below order them as read, read, then (mfma, read) pairs.
+    f32x16 sacc[2];   // S^T of the tile: [kb] keys 32 kb .. + 31, one query per lane
+    bf16x8 pf[2][2];  // P fragments [kb][u]
+    // GEMM0 of one tile: fragment i = (kb, s) read two fragments ahead.
     auto gemm0 = [&](const ATTN_LDS char* kl) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
+        int ka[DS];
+        tile_addr(kl, kofs, ka, DS);
+        constexpr int NF = 2 * DS;
+        bf16x8 kf[4];
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            return *(const ATTN_LDS bf16x8*)at(ka[i % DS], (i / DS) * 32 * T::ROW_BYTES);
+        };
+        kf[0] = rd(0);
+        kf[1] = rd(1);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int s = 0; s < DS; ++s) {
-                const bf16x8 kf = *(const ATTN_LDS bf16x8*)(kl + (koff0 ^ (32 * s)) + kb * 32 * T::ROW_BYTES);
-                sacc[kb] = mfma_bf16(kf, qf[s], s == 0 ? f32x16{} : sacc[kb]);
-            }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * DS - 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < NF; ++i) {
+            const int kb = i / DS, st = i % DS;
+            if (st == 0) mfma_bf16_va0(sacc[kb], kf[i % 4], qf[st]);
+            else mfma_bf16_va(sacc[kb], kf[i % 4], qf[st]);
+            if (i >= 2) keep(kf[(i - 2) % 4]);
+            if (i + 2 < NF) kf[(i + 2) % 4] = rd(i + 2);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        keep(kf[(NF - 2) % 4]);
+        keep(kf[(NF - 1) % 4]);
+        mfma_guard();   // the scores may be read right after
+    };
+    // GEMM1 of one tile: fragment i = (kb, u, t) read two fragments ahead.
+    auto gemm1 = [&](const ATTN_LDS char* vl) __attribute__((always_inline)) {
+        int va[DT];
+        tile_addr(vl, vofs, va, DT);
+        constexpr int NF = 4 * DT;
+        bf16x8 vf[4];
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            const int kb = i / (2 * DT), u = (i / DT) % 2, t = i % DT;
+            const int imm = (32 * kb + 16 * u) * T::ROW_BYTES;
+            const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)at(va[t], imm));
+            const bf16x4 hi4 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)at(va[t], imm + 8 * T::ROW_BYTES));
+            return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        vf[0] = rd(0);
+        vf[1] = rd(1);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int kb = i / (2 * DT), u = (i / DT) % 2, t = i % DT;
+            mfma_bf16_a(o[t], vf[i % 4], pf[kb][u]);
+            if (i >= 2) keep(vf[(i - 2) % 4]);
+            if (i + 2 < NF) vf[(i + 2) % 4] = rd(i + 2);
+        }
+        keep(vf[(NF - 2) % 4]);
+        keep(vf[(NF - 1) % 4]);
+        keep(pf[1][0]);
+        keep(pf[1][1]);
     };
 
     auto is_full = [&](int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) -> bool {
@@ -205,55 +271,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         return full;
     };
 
-    bf16x8 pf[2][2];
-    float rescale_by = 1.f;      // output factor of the last softmax (1 for most rows)
-    bool rescale_any = false;    // some row of the wave needs it
-    // Online-softmax update shared by both softmax variants: new reference max,
-    // rescale factor, then p = exp2(y - m) into bf16 P and the running sum. The
-    // reference only moves when the row max grew by more than 2^kLazyTau.
-    auto finish = [&](float mx, auto&& ys) __attribute__((always_inline)) {
-        const float mold = m;
-        const float mn = fmaxf(mold, mx);
-        const bool upd = mold == -INFINITY || mn > mold + kLazyTau;
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = upd ? fast_exp2(mold - mref) : 1.f;
-        const bool need = upd && mold != -INFINITY;
-        m = upd ? mn : mold;
-        const float mu = m == -INFINITY ? 0.f : m;
-        float ls0 = 0.f, ls1 = 0.f, ls2 = 0.f, ls3 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(ys(kb, r, mu)), p1 = fast_exp2(ys(kb, r + 1, mu));
-                if (r & 2) { ls2 += p0; ls3 += p1; } else { ls0 += p0; ls1 += p1; }
-                pf[kb][r >> 3][(r & 7)] = (__bf16)p0;
-                pf[kb][r >> 3][(r & 7) + 1] = (__bf16)p1;
-            }
-        l = l * alpha + ((ls0 + ls1) + (ls2 + ls3));
-        rescale_by = need ? alpha : 1.f;
-        rescale_any = __builtin_amdgcn_ballot_w64(need) != 0;
-    };
-
-    // Full tile, no score modifier: the max is taken on raw q.k and the scale
-    // is folded into the exponent argument, one FMA per score.
-    auto softmax_plain = [&]() __attribute__((always_inline)) {
-        float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) {
-            a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
-            a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
-        }
-        a0 = max3(a0, sacc[0][15], a1);
-        const float mx = xhalf_max(fmaxf(a0, sacc[1][15])) * c;
-        finish(mx, [&](int kb, int r, float mu) __attribute__((always_inline)) {
-            return __builtin_fmaf(sacc[kb][r], c, -mu);
-        });
-    };
-
-    // Score modifiers and / or the element mask (partial tiles): the modified
-    // score in exp2 units replaces the raw one, masked entries become -inf.
-    auto softmax_general = [&](bool full, int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
+    // Score modifiers and / or the element mask, in place: the scores become
+    // exp2-unit values, -inf where the key is not allowed for the row.
+    auto prepare_scores = [&](bool full, int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
         const int j0 = kt * BN;
         int dk[2][16];
         if (DOC && !full) {
@@ -269,67 +289,86 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         // allowed keys of this row within the tile: jl_lo <= jl <= jl_hi
         const int jl_hi = full ? BN : min(Nk - 1 - j0, causal ? row + off - j0 : INT_MAX / 2);
         const int jl_lo = (windowed && !full) ? row + off - W + 1 - j0 : 0;
-        const bool mask_doc = DOC && !full;
-        float a0 = -INFINITY, a1 = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
-                float y;
-                if (SOFTCAP) {
-                    // cap * tanh(x / cap) = cap - 2 cap / (exp(2 x / cap) + 1), in exp2 units
-                    const float e = fast_exp2(sacc[kb][r] * cap_in);
-                    y = cap_l2 - 2.f * cap_l2 * fast_rcp(e + 1.f);
-                } else {
-                    y = sacc[kb][r] * c;
-                }
-                if (ALIBI) y -= slope_l2 * (float)(row - (j0 + jl));
-                bool ok = jl <= jl_hi && jl >= jl_lo;
-                if (DOC) ok &= !mask_doc || dk[kb][r] == doc_i;
-                y = ok ? y : -INFINITY;
-                sacc[kb][r] = y;
-                if (kb == 0) a0 = fmaxf(a0, y); else a1 = fmaxf(a1, y);
-            }
-        }
-        const float mx = xhalf_max(fmaxf(a0, a1));
-        finish(mx, [&](int kb, int r, float mu) __attribute__((always_inline)) { return sacc[kb][r] - mu; });
-    };
-
-    auto softmax = [&](bool full, int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
-        if (!MODS && full) softmax_plain();
-        else softmax_general(full, kt, dl);
-    };
-
-
-    auto gemm1 = [&](const ATTN_LDS char* vl) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int t = 0; t < DT; ++t) {
-                    const int base = (32 * kb + 16 * u) * T::ROW_BYTES + (voff0 ^ (64 * t));
-                    const bf16x4 lo4 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)(vl + base));
-                    const bf16x4 hi4 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)(vl + base + 8 * T::ROW_BYTES));
-                    const bf16x8 vf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[t] = mfma_bf16(vf, pf[kb][u], o[t]);
+            for (int r = 0; r < 16; ++r) {
+                const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
+                if ((r & 3) == 0) pin(sacc[kb]);   // four elements at a time
+                const float x = sacc[kb][r];
+                float y;
+                if (SOFTCAP) {
+                    // cap * tanh(x / cap) = cap - 2 cap / (exp(2 x / cap) + 1), in exp2 units
+                    const float e = fast_exp2(x * cap_in);
+                    y = cap_l2 - 2.f * cap_l2 * fast_rcp(e + 1.f);
+                } else {
+                    y = x * c;
                 }
-        constexpr int NM = 4 * DT;   // matrix instructions in this phase
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < NM - 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
+                if (ALIBI) y -= slope_l2 * (float)(row - (j0 + jl));
+                bool ok = jl <= jl_hi && jl >= jl_lo;
+                if (DOC && !full) ok &= dk[kb][r] == doc_i;
+                sacc[kb][r] = ok ? y : -INFINITY;
+            }
     };
 
-    auto in_w = [&](int kt) __attribute__((always_inline)) { return kt >= wt_begin && kt < wt_end; };
+    float rescale_by = 1.f;      // output factor of the last softmax (1 for most rows)
+    bool rescale_any = false;    // some row of the wave needs it
+    // Online softmax of tile kt: scores -> P, running max / sum. Plain full
+    // tiles keep raw scores (scale folded into the exponent FMA).
+    auto softmax = [&](int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
+        const bool full = is_full(kt, dl);
+        const bool pre = MODS || !full || !(c > 0.f);
+        if (pre) prepare_scores(full, kt, dl);
+        const float ce = pre ? 1.f : c;
+        float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) {
+            a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
+            a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
+        }
+        a0 = max3(a0, sacc[0][15], max2(a1, sacc[1][15]));
+        const float mx = xhalf_max(a0) * ce;
+        const float mn = max2(m, mx);
+        const bool need = mn > m + kLazyTau;
+        const float alpha = need ? fast_exp2(m - mn) : 1.f;
+        m = need ? mn : m;
+        const float mneg = -m;
+        float ls0 = 0.f, ls1 = 0.f, ls2 = 0.f, ls3 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][r], ce, mneg));
+                const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r + 1], ce, mneg));
+                if (r & 2) { ls2 += p0; ls3 += p1; } else { ls0 += p0; ls1 += p1; }
+                pf[kb][r >> 3][(r & 7)] = (__bf16)p0;
+                pf[kb][r >> 3][(r & 7) + 1] = (__bf16)p1;
+            }
+        // P is complete here; GEMM1 reads it only after the wait states below
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            pin(pf[kb][0]);
+            pin(pf[kb][1]);
+        }
+        l = l * alpha + ((ls0 + ls1) + (ls2 + ls3));
+        rescale_by = alpha;
+        rescale_any = __builtin_amdgcn_ballot_w64(need) != 0;
+        if (__builtin_expect(rescale_any, 0)) {   // rare: the reference max moved
+            mfma_guard();
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                // one output tile at a time through VGPRs
+                pin_a(o[t]);
+                f32x16 x = o[t];
+                pin(x);
+                x *= rescale_by;
+                o[t] = x;
+                pin_a(o[t]);
+            }
+            mfma_guard();
+        }
+    };
+
     Copy copy;
     copy.init(wave, lane);
     auto tile_k = [&](int i) __attribute__((always_inline)) {
@@ -340,12 +379,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         if (DOC) issue_docs(docrow, (kt_begin + i) * BN, Nk, lds_addr(dbuf(i)), wave, lane);
     };
 
-    // ---------------------------------------------------------------- ping-pong loop
-    // Barrier i (i >= 1) is passed by group B at the top of body(i - 1) and by
-    // group A in the middle of body(i - 1). Before it, each wave waits for its
-    // copies of tile i only (tile i + 1 may still be in flight when PF = 2);
-    // after it, it issues its share of tile i + PF. Between barriers i and i + 1
-    // the waves read K(i), V(i - 1) and V(i), never a buffer being refilled.
+    // ---------------------------------------------------------------- ping-pong loops
+    // Barrier i (i >= 1) is passed by group B at the top of iteration i - 1
+    // and by group A in its middle. Before it, each wave waits for its copies
+    // of tile i only (tile i + 1 may still be in flight when PF = 2); after
+    // it, it issues its share of tile i + PF. Between barriers i and i + 1 the
+    // waves read K(i), V(i - 1) and V(i), never a buffer being refilled.
     auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
         if (PF >= 2 && i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
@@ -357,6 +396,24 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
             tile_v(i + PF);
         }
     };
+    // Iteration it over a tile of this wave's key range: softmax and GEMM1 of
+    // tile it, GEMM0 of tile it + 1 (when it is also in the range).
+    auto body = [&](int it, bool next) __attribute__((always_inline)) {
+        const int kt = kt_begin + it;
+        if (group_b) barrier_and_copy(it + 1);
+        softmax(kt, dbuf(it));
+        mfma_guard();   // P was written by vector code just before
+        gemm1(vbuf(it));
+        if (!group_b) barrier_and_copy(it + 1);
+        if (next) gemm0(kbuf(it + 1));
+    };
+
+    // this wave's tiles: [wb, we) relative to kt_begin
+    int wb = n_tiles, we = n_tiles;
+    if (wt_end > wt_begin) {
+        wb = wt_begin - kt_begin;
+        we = wt_end - kt_begin;
+    }
     if (n_tiles > 0) {
 #pragma unroll
         for (int i = 0; i < PF; ++i)
@@ -365,26 +422,23 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
                 tile_v(i);
             }
         barrier_and_copy(0);
-        if (in_w(kt_begin)) gemm0(kbuf(0));
     }
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const int kt = kt_begin + it;
-        if (group_b) barrier_and_copy(it + 1);
-        if (in_w(kt)) {
-            softmax(is_full(kt, dbuf(it)), kt, dbuf(it));
-            if (__builtin_expect(rescale_any, 0)) {   // rare: the reference max moved
-#pragma unroll
-                for (int t = 0; t < DT; ++t) o[t] *= rescale_by;
-            }
-            gemm1(vbuf(it));
+    int it = 0;
+    if (wb < we) {
+        if (wb == 0) gemm0(kbuf(0));
+        for (; it < wb; ++it) {   // before the range: barriers and copies only
+            barrier_and_copy(it + 1);
+            if (it + 1 == wb) gemm0(kbuf(wb));
         }
-        if (!group_b) barrier_and_copy(it + 1);
-        if (it + 1 < n_tiles && in_w(kt + 1)) gemm0(kbuf(it + 1));
+        for (; it < we - 1; ++it) body(it, true);
+        body(it, false);
+        ++it;
     }
+    for (; it < n_tiles; ++it) barrier_and_copy(it + 1);   // after the range
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
     if (!wave_active) return;
+    mfma_guard();
     __bf16* O = (__bf16*)p.o + (size_t)(b * p.Hq + h) * Nq * D;
     const float lt = xhalf_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;

@@ -88,6 +88,44 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product issued as inline assembly with the register file of each
+// operand fixed: "v" keeps a value in VGPRs (read by vector code), "a" in
+// AGPRs (touched only by the matrix core). The compiler does not see these as
+// matrix instructions, so the caller keeps every vector access to their
+// registers away from them: results are read (and AGPRs read or written by
+// vector code) at least mfma_guard() after the instruction, operands written
+// by vector code are written well before it, and source registers stay
+// allocated (keep) for a few instructions after it.
+__device__ __forceinline__ void mfma_bf16_va(f32x16& c, bf16x8 a, bf16x8 b) {   // c += a b, b in AGPRs
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_va0(f32x16& c, bf16x8 a, bf16x8 b) {  // c = a b, b in AGPRs
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_a(f32x16& c, bf16x8 a, bf16x8 b) {    // c += a b, c in AGPRs
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 32 wait states: more than a 32x32x16 product needs before its result may be
+// read by vector code or its AGPRs accessed with v_accvgpr_read / write.
+__device__ __forceinline__ void mfma_guard() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+// Pins a value at this point of the instruction stream (an empty volatile
+// statement that reads and rewrites it), so work placed around it stays there.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+    asm volatile("" : "+v"(x));
+}
+template <typename T>
+__device__ __forceinline__ void pin_a(T& x) {   // same for a value in AGPRs
+    asm volatile("" : "+a"(x));
+}
+// Keeps a value (and its registers) allocated up to this point.
+template <typename T>
+__device__ __forceinline__ void keep(const T& x) {
+    asm volatile("" :: "v"(x));
+}
+
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -101,6 +139,13 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 __device__ __forceinline__ float max3(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max(a, b) in one instruction (no operand canonicalization).
+__device__ __forceinline__ float max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
     return r;
 }
 
