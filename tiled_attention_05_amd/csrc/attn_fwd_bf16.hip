@@ -193,9 +193,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // Per-lane fragment addresses of one tile: the tile base is added once
     // and pinned there; the kb / u / row-half parts are immediate offsets.
     auto tile_addr = [&](const ATTN_LDS char* base, const int* ofs, int* a, int n) __attribute__((always_inline)) {
+        // one scalar base (the buffer index arithmetic stays on the scalar unit)
+        const int sb = __builtin_amdgcn_readfirstlane((int)lds_addr(base));
 #pragma unroll
         for (int i = 0; i < n; ++i) {
-            a[i] = (int)lds_addr(base) + ofs[i];
+            a[i] = sb + ofs[i];
             pin(a[i]);
         }
     };
