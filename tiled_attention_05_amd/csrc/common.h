@@ -105,8 +105,19 @@ __device__ __forceinline__ void mfma_bf16_va0(f32x16& c, bf16x8 a, bf16x8 b) {  
 __device__ __forceinline__ void mfma_bf16_a(f32x16& c, bf16x8 a, bf16x8 b) {    // c += a b, c in AGPRs
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
-// 32 wait states: more than a 32x32x16 product needs before its result may be
-// read by vector code or its AGPRs accessed with v_accvgpr_read / write.
+// e4m3 x e4m3 -> f32 32x32x64 products in the same form (unscaled encoding).
+__device__ __forceinline__ void mfma_fp8_va(f32x16& c, i32x8 a, i32x8 b) {    // c += a b, b in AGPRs
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_fp8_va0(f32x16& c, i32x8 a, i32x8 b) {   // c = a b, b in AGPRs
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_fp8_a(f32x16& c, i32x8 a, i32x8 b) {     // c += a b, c in AGPRs
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 32 wait states: more than a 32x32x16 bf16 or 32x32x64 e4m3 product needs
+// before its result may be read by vector code or its AGPRs accessed with
+// v_accvgpr_read / write.
 __device__ __forceinline__ void mfma_guard() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }

@@ -15,6 +15,8 @@
 
 namespace attn {
 
+constexpr float kFp8NoMax = -1e30f;   // initial exponent reference: finite, below any score
+
 constexpr int kFp8Tile = 128;        // tokens per quantisation scale
 constexpr float kE4m3Max = 448.f;
 constexpr float kFp8PShift = 4.f;    // P is stored as e4m3(p * 2^4 * s_v / s_vmax), p <= 2^4
@@ -216,15 +218,37 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     f32x16 o[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[t] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    float m = kFp8NoMax, l = 0.f;
+    // Matrix operands written by vector code: set here, pinned in their
+    // register files, followed by wait states before the first product.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) pin_a(qf[s]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pin_a(o[t]);
+    mfma_guard();
 
-    // K reads: block kb, lane row pi(l32) (+16 kb), 16-byte chunks 4 s + 2 hh + {0, 1}
-    const int krow = 32 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
-    // V^T reads: row 32 t + l32, 16-byte chunks 2 hh + {0, 1}
     ATTN_LDS char* lds = (ATTN_LDS char*)tiles_lds;
     auto kbuf = [&](int i) __attribute__((always_inline)) { return lds + (i % NKB) * T::KBYTES; };
     auto vbuf = [&](int i) __attribute__((always_inline)) {
         return lds + NKB * T::KBYTES + (i % NVB) * T::VBYTES;
+    };
+    // Lane-constant fragment offsets. K: block kb, lane row pi(l32) (+16 kb),
+    // 16-byte chunks 4 s + 2 hh + {0, 1}. V^T: row 32 t + l32 (the swizzle
+    // does not depend on t), 16-byte chunks 2 hh + {0, 1}.
+    const int krow = 32 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
+    int kofs[2][2][2], vofs[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int r = krow + 16 * kb, sw = T::swz_k(r);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) kofs[kb][st][hf] = r * T::KROW + (((4 * st + 2 * hh + hf) ^ sw) << 4);
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) vofs[hf] = l32 * T::VROW + (((2 * hh + hf) ^ T::swz_v(l32)) << 4);
+    auto at = [](int addr, int imm) __attribute__((always_inline)) {
+        return (const ATTN_LDS char*)(uintptr_t)addr + imm;
     };
 
     // tile copies: one 16-byte slot per lane per tile, for K and for V^T
@@ -242,25 +266,35 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
 
     f32x16 sacc[2];
     auto gemm0 = [&](const ATTN_LDS char* kl) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
+        const int sb = __builtin_amdgcn_readfirstlane((int)lds_addr(kl));
+        int ka[2][2][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int r = krow + 16 * kb;
-            const ATTN_LDS char* rb = kl + r * T::KROW;
-            const int sw = T::swz_k(r);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int c0 = 4 * s + 2 * hh;
-                const i32x4 lo = *(const ATTN_LDS i32x4*)(rb + ((c0 ^ sw) << 4));
-                const i32x4 hi = *(const ATTN_LDS i32x4*)(rb + (((c0 + 1) ^ sw) << 4));
-                const i32x8 kf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                sacc[kb] = mfma_fp8(kf, qf[s], s == 0 ? f32x16{} : sacc[kb]);
-            }
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    ka[kb][st][hf] = sb + kofs[kb][st][hf];
+                    pin(ka[kb][st][hf]);
+                }
+        i32x8 kf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {   // i = (kb, st)
+            const i32x4 lo = *(const ATTN_LDS i32x4*)at(ka[i >> 1][i & 1][0], 0);
+            const i32x4 hi = *(const ATTN_LDS i32x4*)at(ka[i >> 1][i & 1][1], 0);
+            kf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if ((i & 1) == 0) mfma_fp8_va0(sacc[i >> 1], kf[i], qf[0]);
+            else mfma_fp8_va(sacc[i >> 1], kf[i], qf[1]);
+        }
+        mfma_guard();   // the scores may be read right after
+#pragma unroll
+        for (int i = 0; i < 4; ++i) keep(kf[i]);
     };
 
-    i32x8 pf;
+    i32x8 pf = {};
     float rescale_by = 1.f;
     bool rescale_any = false;
     auto softmax = [&](int it) __attribute__((always_inline)) {
@@ -268,36 +302,28 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
         const float c = c_q * ksc_s[tsc];                        // score multiplier, exp2 units
         const float bias = kFp8PShift + __builtin_amdgcn_logf(vsc_s[tsc]) - log2_svmax;
         const int jl_hi = RAGGED ? N - 1 - it * BN : BN;         // last valid key in the tile
-        float mx;
-        if (!RAGGED || jl_hi >= BN - 1) {
-            float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
-#pragma unroll
-            for (int r = 3; r < 15; r += 2) {
-                a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
-                a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
-            }
-            mx = xhalf_max(max3(a0, sacc[0][15], fmaxf(a1, sacc[1][15]))) * c;
-        } else {
-            float a = -INFINITY;
+        if (RAGGED && jl_hi < BN - 1) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int jl = 32 * hh + 16 * kb + r;
                     sacc[kb][r] = jl <= jl_hi ? sacc[kb][r] : -INFINITY;
-                    a = fmaxf(a, sacc[kb][r]);
                 }
-            mx = xhalf_max(a) * c;
         }
-        const float mold = m;
-        const float mn = fmaxf(mold, mx);
-        const bool upd = mold == -INFINITY || mn > mold + kTau;
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = upd ? fast_exp2(mold - mref) : 1.f;
-        const bool need = upd && mold != -INFINITY;
-        m = upd ? mn : mold;
-        const float mb = (m == -INFINITY ? 0.f : m) - bias;
-        float ls0 = 0.f, ls1 = 0.f, ls2 = 0.f, ls3 = 0.f;
+        float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) {
+            a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
+            a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
+        }
+        const float mx = xhalf_max(max3(a0, sacc[0][15], max2(a1, sacc[1][15]))) * c;
+        const float mn = max2(m, mx);
+        const bool need = mn > m + kTau;
+        const float alpha = need ? fast_exp2(m - mn) : 1.f;
+        m = need ? mn : m;
+        const float mb = m - bias;
+        float ls0, ls1, ls2, ls3;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -306,30 +332,61 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
                 const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r + 1], c, -mb));
                 const float p2 = fast_exp2(__builtin_fmaf(sacc[kb][r + 2], c, -mb));
                 const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][r + 3], c, -mb));
-                ls0 += p0; ls1 += p1; ls2 += p2; ls3 += p3;
-                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                pf[4 * kb + (r >> 2)] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, pk, true);
+                if (kb == 0 && r == 0) {
+                    ls0 = p0; ls1 = p1; ls2 = p2; ls3 = p3;
+                } else {
+                    ls0 += p0; ls1 += p1; ls2 += p2; ls3 += p3;
+                }
+                // both halves of the word are written: the old contents only
+                // name the register
+                const int w = 4 * kb + (r >> 2);
+                const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf[w], false);
+                pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, pk, true);
             }
+        pin(pf);   // P is complete here; GEMM1 reads it after wait states
         l = l * alpha + ((ls0 + ls1) + (ls2 + ls3)) * fast_exp2(-bias);
-        rescale_by = need ? alpha : 1.f;
+        rescale_by = alpha;
         rescale_any = __builtin_amdgcn_ballot_w64(need) != 0;
+        if (__builtin_expect(rescale_any, 0)) {   // rare: the reference max moved
+            mfma_guard();
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                // one output tile at a time through VGPRs
+                pin_a(o[t]);
+                f32x16 x = o[t];
+                pin(x);
+                x *= rescale_by;
+                o[t] = x;
+                pin_a(o[t]);
+            }
+            mfma_guard();
+        }
     };
 
     auto gemm1 = [&](const ATTN_LDS char* vl) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
+        const int sb = __builtin_amdgcn_readfirstlane((int)lds_addr(vl));
+        int va[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            va[hf] = sb + vofs[hf];
+            pin(va[hf]);
+        }
+        i32x8 vf[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int r = 32 * t + l32;
-            const ATTN_LDS char* rb = vl + r * T::VROW;
-            const int sw = T::swz_v(r);
-            const i32x4 lo = *(const ATTN_LDS i32x4*)(rb + (((2 * hh) ^ sw) << 4));
-            const i32x4 hi = *(const ATTN_LDS i32x4*)(rb + (((2 * hh + 1) ^ sw) << 4));
-            const i32x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[t] = mfma_fp8(vf, pf, o[t]);
+            const i32x4 lo = *(const ATTN_LDS i32x4*)at(va[0], 32 * t * T::VROW);
+            const i32x4 hi = *(const ATTN_LDS i32x4*)at(va[1], 32 * t * T::VROW);
+            vf[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mfma_fp8_a(o[t], vf[t], pf);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) keep(vf[t]);
+        keep(pf);
     };
 
+    // Barrier i (i >= 1) is passed by group B at the top of iteration i - 1
+    // and by group A in its middle; see the bf16 kernel for the buffer reuse.
     auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
         if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
@@ -341,6 +398,14 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
             tile_v(i + PF);
         }
     };
+    auto body = [&](int it, bool next) __attribute__((always_inline)) {
+        if (group_b) barrier_and_copy(it + 1);
+        softmax(it);
+        mfma_guard();   // P was written by vector code just before
+        gemm1(vbuf(it));
+        if (!group_b) barrier_and_copy(it + 1);
+        if (next) gemm0(kbuf(it + 1));
+    };
 
     if (n_tiles > 0) {
         tile_k(0);
@@ -350,23 +415,20 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
             tile_v(1);
         }
         barrier_and_copy(0);
-        if (wave_active) gemm0(kbuf(0));
     }
-    for (int it = 0; it < n_tiles; ++it) {
-        if (group_b) barrier_and_copy(it + 1);
-        if (wave_active) {
-            softmax(it);
-            if (__builtin_expect(rescale_any, 0)) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] *= rescale_by;
-            }
-            gemm1(vbuf(it));
+    if (wave_active) {
+        if (n_tiles > 0) {
+            gemm0(kbuf(0));
+            int it = 0;
+            for (; it < n_tiles - 1; ++it) body(it, true);
+            body(it, false);
         }
-        if (!group_b) barrier_and_copy(it + 1);
-        if (wave_active && it + 1 < n_tiles) gemm0(kbuf(it + 1));
+    } else {
+        for (int it = 0; it < n_tiles; ++it) barrier_and_copy(it + 1);   // copies and barriers only
     }
 
     if (!wave_active) return;
+    mfma_guard();
     const float lt = xhalf_sum(l);
     const float inv = lt > 0.f ? svmax / (exp2f(kFp8PShift) * lt) : 0.f;
     if (row < N) {
@@ -384,6 +446,9 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
             p.lse[bhq * N + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     }
 }
+
+template __global__ void fwd_fp8_kernel<false>(FwdParams);
+template __global__ void fwd_fp8_kernel<true>(FwdParams);
 
 hipError_t launch_fwd_fp8(const FwdParams& p0, int d, hipStream_t st) {
     if (d != 128) return hipErrorNotSupported;
