@@ -55,6 +55,9 @@
 
 #include "fwd_common.h"
 
+#ifndef ATTN_LDS_AHEAD
+#define ATTN_LDS_AHEAD 4   // matrix fragments read from LDS ahead of their product
+#endif
 #ifndef ATTN_PREFETCH
 #define ATTN_PREFETCH 2   // key/value tiles in flight ahead of the matrix work (1..3)
 #endif
@@ -75,8 +78,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // Copies run PF tiles ahead of the matrix work; key tiles need PF + 1
     // buffers, value tiles (read during two consecutive intervals) PF + 2.
     constexpr int PF = ATTN_PREFETCH;
-    static_assert(PF >= 1 && PF <= 2, "prefetch distance 1 or 2");
+    static_assert(PF >= 1 && PF <= 3, "prefetch distance 1 to 3");
     constexpr int NKB = PF + 1, NVB = PF + 2;
+    // LDS fragments are read LA products ahead of their use; a fragment
+    // register is refilled two products after the product that read it.
+    constexpr int LA = ATTN_LDS_AHEAD, NB = LA + 2;
+    static_assert(LA >= 1 && LA <= 7, "read-ahead 1..7 (lgkmcnt range)");
     using Copy = TileCopy<D, NW>;
     constexpr int LOADS_PER_TILE = 2 * Copy::ROUNDS + (DOC ? 1 : 0);   // per wave
 
@@ -213,30 +220,32 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         int ka[DS];
         tile_addr(kl, kofs, ka, DS);
         constexpr int NF = 2 * DS;
-        bf16x8 kf[4];
+        bf16x8 kf[NB];
         auto rd = [&](int i) __attribute__((always_inline)) {
             return *(const ATTN_LDS bf16x8*)at(ka[i % DS], (i / DS) * 32 * T::ROW_BYTES);
         };
-        kf[0] = rd(0);
-        kf[1] = rd(1);
+#pragma unroll
+        for (int f = 0; f < LA && f < NF; ++f) kf[f] = rd(f);
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
             const int kb = i / DS, st = i % DS;
-            if (st == 0) mfma_bf16_va0(sacc[kb], kf[i % 4], qf[st]);
-            else mfma_bf16_va(sacc[kb], kf[i % 4], qf[st]);
-            if (i >= 2) keep(kf[(i - 2) % 4]);
-            if (i + 2 < NF) kf[(i + 2) % 4] = rd(i + 2);
+            if (st == 0) mfma_bf16_va0(sacc[kb], kf[i % NB], qf[st]);
+            else mfma_bf16_va(sacc[kb], kf[i % NB], qf[st]);
+            if (i >= 2) keep(kf[(i - 2) % NB]);
+            if (i + LA < NF) kf[(i + LA) % NB] = rd(i + LA);
         }
-        keep(kf[(NF - 2) % 4]);
-        keep(kf[(NF - 1) % 4]);
+        keep(kf[(NF - 2) % NB]);
+        keep(kf[(NF - 1) % NB]);
         mfma_guard();   // the scores may be read right after
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pin(sacc[kb]);
     };
     // GEMM1 of one tile: fragment i = (kb, u, t) read two fragments ahead.
     auto gemm1 = [&](const ATTN_LDS char* vl) __attribute__((always_inline)) {
         int va[DT];
         tile_addr(vl, vofs, va, DT);
         constexpr int NF = 4 * DT;
-        bf16x8 vf[4];
+        bf16x8 vf[NB];
         auto rd = [&](int i) __attribute__((always_inline)) {
             const int kb = i / (2 * DT), u = (i / DT) % 2, t = i % DT;
             const int imm = (32 * kb + 16 * u) * T::ROW_BYTES;
@@ -245,17 +254,17 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
                 __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)at(va[t], imm + 8 * T::ROW_BYTES));
             return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         };
-        vf[0] = rd(0);
-        vf[1] = rd(1);
+#pragma unroll
+        for (int f = 0; f < LA && f < NF; ++f) vf[f] = rd(f);
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
             const int kb = i / (2 * DT), u = (i / DT) % 2, t = i % DT;
-            mfma_bf16_a(o[t], vf[i % 4], pf[kb][u]);
-            if (i >= 2) keep(vf[(i - 2) % 4]);
-            if (i + 2 < NF) vf[(i + 2) % 4] = rd(i + 2);
+            mfma_bf16_a(o[t], vf[i % NB], pf[kb][u]);
+            if (i >= 2) keep(vf[(i - 2) % NB]);
+            if (i + LA < NF) vf[(i + LA) % NB] = rd(i + LA);
         }
-        keep(vf[(NF - 2) % 4]);
-        keep(vf[(NF - 1) % 4]);
+        keep(vf[(NF - 2) % NB]);
+        keep(vf[(NF - 1) % NB]);
         keep(pf[1][0]);
         keep(pf[1][1]);
     };
@@ -382,14 +391,20 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     };
 
     // ---------------------------------------------------------------- ping-pong loops
-    // Barrier i (i >= 1) is passed by group B at the top of iteration i - 1
-    // and by group A in its middle. Before it, each wave waits for its copies
-    // of tile i only (tile i + 1 may still be in flight when PF = 2); after
-    // it, it issues its share of tile i + PF. Between barriers i and i + 1 the
-    // waves read K(i), V(i - 1) and V(i), never a buffer being refilled.
+    // Barrier i (i >= 1) is passed by group B at the top of iteration i - 1,
+    // by group A between its softmax and GEMM1 of tile i - 1: on each SIMD one
+    // wave's products (GEMM1 of tile i - 1, GEMM0 of tile i) then overlap the
+    // other wave's softmax. Before the barrier each wave waits for its copies
+    // of tile i only (up to PF - 1 later tiles may stay in flight); after it,
+    // it issues its share of tile i + PF. Between barriers i and i + 1 the
+    // waves read K(i), V(i - 1), the document ids of tiles i - 1 and i, and
+    // refill K(i - 1), V(i - 2): never a buffer being read.
     auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        if (PF >= 2 && i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
+        static_assert(2 * LOADS_PER_TILE <= 15, "vmcnt immediate");
+        const int ahead = min(PF - 1, n_tiles - 1 - i);   // later tiles whose copies may stay in flight
+        if (PF >= 3 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * LOADS_PER_TILE));
+        else if (PF >= 2 && ahead >= 1) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
         else __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -404,9 +419,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         const int kt = kt_begin + it;
         if (group_b) barrier_and_copy(it + 1);
         softmax(kt, dbuf(it));
-        mfma_guard();   // P was written by vector code just before
-        gemm1(vbuf(it));
         if (!group_b) barrier_and_copy(it + 1);
+        mfma_guard();   // P was written by vector code just before
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            pin(pf[kb][0]);
+            pin(pf[kb][1]);
+        }
+        gemm1(vbuf(it));
         if (next) gemm0(kbuf(it + 1));
     };
 
@@ -441,6 +461,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
     if (!wave_active) return;
     mfma_guard();
+#pragma unroll
+    for (int t = 0; t < DT; ++t) pin_a(o[t]);
     __bf16* O = (__bf16*)p.o + (size_t)(b * p.Hq + h) * Nq * D;
     const float lt = xhalf_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;

@@ -117,7 +117,10 @@ __device__ __forceinline__ void mfma_fp8_a(f32x16& c, i32x8 a, i32x8 b) {     //
 }
 // 32 wait states: more than a 32x32x16 bf16 or 32x32x64 e4m3 product needs
 // before its result may be read by vector code or its AGPRs accessed with
-// v_accvgpr_read / write.
+// v_accvgpr_read / write. The guard orders only against other volatile asm:
+// plain register reads may still be scheduled above it, so every value read
+// after a guard is re-pinned (pin / pin_a) right after it, which makes its
+// readers depend on a statement that follows the wait states.
 __device__ __forceinline__ void mfma_guard() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }

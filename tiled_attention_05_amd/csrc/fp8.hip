@@ -291,6 +291,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
         }
         mfma_guard();   // the scores may be read right after
 #pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pin(sacc[kb]);
+#pragma unroll
         for (int i = 0; i < 4; ++i) keep(kf[i]);
     };
 
@@ -386,7 +388,9 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     };
 
     // Barrier i (i >= 1) is passed by group B at the top of iteration i - 1
-    // and by group A in its middle; see the bf16 kernel for the buffer reuse.
+    // and by group A between its softmax and GEMM1 of tile i - 1, so that one
+    // wave's products overlap the other's softmax on each SIMD; the buffer
+    // reuse argument is the bf16 kernel's.
     auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
         if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
@@ -401,9 +405,10 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     auto body = [&](int it, bool next) __attribute__((always_inline)) {
         if (group_b) barrier_and_copy(it + 1);
         softmax(it);
-        mfma_guard();   // P was written by vector code just before
-        gemm1(vbuf(it));
         if (!group_b) barrier_and_copy(it + 1);
+        mfma_guard();   // P was written by vector code just before
+        pin(pf);
+        gemm1(vbuf(it));
         if (next) gemm0(kbuf(it + 1));
     };
 
@@ -429,6 +434,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
 
     if (!wave_active) return;
     mfma_guard();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pin_a(o[t]);
     const float lt = xhalf_sum(l);
     const float inv = lt > 0.f ? svmax / (exp2f(kFp8PShift) * lt) : 0.f;
     if (row < N) {
