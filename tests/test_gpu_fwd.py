@@ -72,6 +72,19 @@ def test_small_parity(label, w, docs):
     _check(w, _case(w, doc_range=docs), label)
 
 
+def test_softcap_polynomial_and_exact_tiles():
+    """Soft-cap 50 with Q scaled by 6: 42 of the 980000 scores have
+    |scale q.k| > 25, beyond the range of the kernel's polynomial form, so a
+    few wave tiles take the exact form and the rest the polynomial in one
+    launch."""
+    w = I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=700, mask=0, softcap=50.0)
+    x = I.inputs(w, seed=5)
+    x["q"] = (x["q"].float() * 6).to(x["q"].dtype)
+    s = (x["q"].float() @ x["k"].float().transpose(-1, -2)) * w.scale
+    assert 0 < (s.abs() > 25).sum() < s.numel() // 1000
+    _check(w, x, "softcap both forms")
+
+
 @pytest.mark.parametrize("N", [1, 5, 63, 64, 65, 255, 257])
 @pytest.mark.parametrize("mask", [0, C])
 def test_short_sequences(N, mask):

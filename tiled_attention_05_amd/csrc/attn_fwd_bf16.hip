@@ -55,6 +55,14 @@
 
 #include "fwd_common.h"
 
+namespace attn {
+// Degree-3 fit of tanh(u) / u in t = u^2 on |u| <= kTanhPolyU (weighted least
+// squares on Chebyshev nodes, reweighted toward equal relative error).
+constexpr float kTanhPolyU = 0.5f;
+constexpr float kTanhP0 = 0.999999463558197f, kTanhP1 = -0.33326318860054016f;
+constexpr float kTanhP2 = 0.13190290331840515f, kTanhP3 = -0.04440207779407501f;
+}  // namespace attn
+
 #ifndef ATTN_LDS_AHEAD
 #define ATTN_LDS_AHEAD 4   // matrix fragments read from LDS ahead of their product
 #endif
@@ -146,6 +154,19 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
     const float cap_l2 = SOFTCAP ? p.softcap * kLog2e : 0.f;        // cap in exp2 units
     const float cap_in = SOFTCAP ? p.scale * 2.f * kLog2e / p.softcap : 0.f;
+    // Soft-cap on small scores: cap tanh(v / cap) = v P((v / cap)^2) with
+    // v = c x (exp2 units), P a degree-3 fit of tanh(u) / u on |u| <= 1/2
+    // (relative error 6.2e-7 evaluated in float32), its coefficients rescaled
+    // so that P is evaluated at v^2. Used for a tile when every raw score of
+    // the wave satisfies |x| <= tc_xmax.
+    float tc1 = 0.f, tc2 = 0.f, tc3 = 0.f, tc_xmax = 0.f;
+    if (SOFTCAP) {
+        const float k = 1.f / (cap_l2 * cap_l2);
+        tc1 = kTanhP1 * k;
+        tc2 = kTanhP2 * k * k;
+        tc3 = kTanhP3 * k * k * k;
+        tc_xmax = kTanhPolyU * p.softcap / p.scale;
+    }
 
     // ---- Q fragments (B operand of GEMM0): lane holds row l32, d = 16 s + 8 hh + 0..7
     bf16x8 qf[DS];
@@ -300,6 +321,38 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         // allowed keys of this row within the tile: jl_lo <= jl <= jl_hi
         const int jl_hi = full ? BN : min(Nk - 1 - j0, causal ? row + off - j0 : INT_MAX / 2);
         const int jl_lo = (windowed && !full) ? row + off - W + 1 - j0 : 0;
+        if (SOFTCAP) {
+            // cap tanh(x / cap) in exp2 units, in place: the polynomial when
+            // every raw score of the wave is in its range, else the exact form
+            float a0 = max3_abs(sacc[0][0], sacc[0][1], sacc[0][2]);
+            float a1 = max3_abs(sacc[1][0], sacc[1][1], sacc[1][2]);
+#pragma unroll
+            for (int r = 3; r < 15; r += 2) {
+                a0 = max3_abs(a0, sacc[0][r], sacc[0][r + 1]);
+                a1 = max3_abs(a1, sacc[1][r], sacc[1][r + 1]);
+            }
+            a0 = max3_abs(a0, sacc[0][15], a1);
+            a0 = max3_abs(a0, sacc[1][15], sacc[1][15]);
+            if (__builtin_amdgcn_ballot_w64(!(a0 <= tc_xmax)) == 0) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = sacc[kb][r] * c, t = v * v;
+                        sacc[kb][r] = v * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(tc3, t, tc2), t, tc1), t,
+                                                         kTanhP0);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        // cap - 2 cap / (exp(2 x / cap) + 1)
+                        const float e = fast_exp2(sacc[kb][r] * cap_in);
+                        sacc[kb][r] = cap_l2 - 2.f * cap_l2 * fast_rcp(e + 1.f);
+                    }
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -307,14 +360,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
                 const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
                 if ((r & 3) == 0) pin(sacc[kb]);   // four elements at a time
                 const float x = sacc[kb][r];
-                float y;
-                if (SOFTCAP) {
-                    // cap * tanh(x / cap) = cap - 2 cap / (exp(2 x / cap) + 1), in exp2 units
-                    const float e = fast_exp2(x * cap_in);
-                    y = cap_l2 - 2.f * cap_l2 * fast_rcp(e + 1.f);
-                } else {
-                    y = x * c;
-                }
+                float y = SOFTCAP ? x : x * c;
                 if (ALIBI) y -= slope_l2 * (float)(row - (j0 + jl));
                 bool ok = jl <= jl_hi && jl >= jl_lo;
                 if (DOC && !full) ok &= dk[kb][r] == doc_i;

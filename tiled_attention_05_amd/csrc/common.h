@@ -157,6 +157,12 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 }
 
 // max(a, b) in one instruction (no operand canonicalization).
+// max(|a|, |b|, |c|) through the instruction's absolute-value modifiers
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 __device__ __forceinline__ float max2(float a, float b) {
     float r;
     asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
