@@ -66,6 +66,12 @@ constexpr float kTanhP2 = 0.13190290331840515f, kTanhP3 = -0.04440207779407501f;
 #ifndef ATTN_LDS_AHEAD
 #define ATTN_LDS_AHEAD 4   // matrix fragments read from LDS ahead of their product
 #endif
+#ifndef ATTN_LATE_COPY_A
+#define ATTN_LATE_COPY_A 1
+#endif
+#ifndef ATTN_LATE_COPY_B
+#define ATTN_LATE_COPY_B 1
+#endif
 #ifndef ATTN_PREFETCH
 #define ATTN_PREFETCH 2   // key/value tiles in flight ahead of the matrix work (1..3)
 #endif
@@ -445,7 +451,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // it issues its share of tile i + PF. Between barriers i and i + 1 the
     // waves read K(i), V(i - 1), the document ids of tiles i - 1 and i, and
     // refill K(i - 1), V(i - 2): never a buffer being read.
-    auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
+    auto copies = [&](int i) __attribute__((always_inline)) {
+        if (i + PF < n_tiles) {
+            tile_k(i + PF);
+            tile_v(i + PF);
+        }
+    };
+    auto barrier_and_copy = [&](int i, bool copy = true) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
         static_assert(2 * LOADS_PER_TILE <= 15, "vmcnt immediate");
         const int ahead = min(PF - 1, n_tiles - 1 - i);   // later tiles whose copies may stay in flight
@@ -454,18 +466,22 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         else __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (i + PF < n_tiles) {
-            tile_k(i + PF);
-            tile_v(i + PF);
-        }
+        if (copy) copies(i);
     };
+    // Copies of tile i + PF may go out anywhere between barriers i and i + 1.
+    // Issued by all waves right after the barrier they queue up behind each
+    // other (the CU's vector-memory path drains about 64 bytes per cycle) and
+    // hold every wave; in the plain kernel (no modifier, no document ids)
+    // they go out at the end of the interval instead. (The other kernels run
+    // out of registers with the copies there.)
+    constexpr bool LATE_A = ATTN_LATE_COPY_A && !DOC && !MODS, LATE_B = ATTN_LATE_COPY_B && !DOC && !MODS;
     // Iteration it over a tile of this wave's key range: softmax and GEMM1 of
     // tile it, GEMM0 of tile it + 1 (when it is also in the range).
     auto body = [&](int it, bool next) __attribute__((always_inline)) {
         const int kt = kt_begin + it;
-        if (group_b) barrier_and_copy(it + 1);
+        if (group_b) barrier_and_copy(it + 1, !LATE_B);
         softmax(kt, dbuf(it));
-        if (!group_b) barrier_and_copy(it + 1);
+        if (!group_b) barrier_and_copy(it + 1, !LATE_A);
         mfma_guard();   // P was written by vector code just before
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -474,6 +490,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         }
         gemm1(vbuf(it));
         if (next) gemm0(kbuf(it + 1));
+        if (group_b ? LATE_B : LATE_A) copies(it + 1);
     };
 
     // this wave's tiles: [wb, we) relative to kt_begin
