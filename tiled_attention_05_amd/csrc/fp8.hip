@@ -390,26 +390,32 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     // Barrier i (i >= 1) is passed by group B at the top of iteration i - 1
     // and by group A between its softmax and GEMM1 of tile i - 1, so that one
     // wave's products overlap the other's softmax on each SIMD; the buffer
-    // reuse argument is the bf16 kernel's.
-    auto barrier_and_copy = [&](int i) __attribute__((always_inline)) {
-        asm volatile("" ::: "memory");
-        if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
-        else __builtin_amdgcn_s_waitcnt(0x0070);
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+    // reuse argument is the bf16 kernel's. In the loop each wave issues its
+    // copies of tile i + PF at the end of the interval (after its GEMM0), not
+    // right after the barrier where all waves would queue up together.
+    auto copies = [&](int i) __attribute__((always_inline)) {
         if (i + PF < n_tiles) {
             tile_k(i + PF);
             tile_v(i + PF);
         }
     };
+    auto barrier_and_copy = [&](int i, bool copy = true) __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
+        else __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (copy) copies(i);
+    };
     auto body = [&](int it, bool next) __attribute__((always_inline)) {
-        if (group_b) barrier_and_copy(it + 1);
+        if (group_b) barrier_and_copy(it + 1, false);
         softmax(it);
-        if (!group_b) barrier_and_copy(it + 1);
+        if (!group_b) barrier_and_copy(it + 1, false);
         mfma_guard();   // P was written by vector code just before
         pin(pf);
         gemm1(vbuf(it));
         if (next) gemm0(kbuf(it + 1));
+        copies(it + 1);
     };
 
     if (n_tiles > 0) {
