@@ -227,3 +227,28 @@ def allowed_pairs(Nq, Nk, mask_kind, window=0, doc_row=None, chunk=1024):
         r = np.arange(a, min(a + chunk, Nq))
         n += int(allowed_mask(r, cols, Nq, Nk, mask_kind, window, doc_row).sum())
     return n
+
+
+def attention_varlen(q, k, v, cu_seqlens, scale, mask_kind=MASK_NONE, window=0, softcap=0.0,
+                     alibi_slopes=None, threads=None):
+    """Exact forward over a packed batch of sequences, one sequence at a time.
+
+    q [Hq, total, d], k / v [Hkv, total, d]; sequence s is tokens
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends only within itself
+    ("FlashAttention-3 : ...", section "Optimisations restantes et integration
+    future": variable-length sequences). Each sequence is cut out and passed to
+    ``attention`` as a batch of one, with its own positions (mask_kind: NONE or
+    CAUSAL, optionally | WINDOW). Returns (O [Hq, total, d], LSE [Hq, total]).
+    """
+    Hq, total, d = q.shape
+    cu = [int(x) for x in np.asarray(_f64(cu_seqlens)).astype(np.int64)]
+    O = np.zeros((Hq, total, d))
+    L = np.full((Hq, total), -np.inf)
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b <= a:
+            continue
+        o, l = attention(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], scale, mask_kind, window,
+                         None, softcap, alibi_slopes, threads=threads)
+        O[:, a:b] = o[0]
+        L[:, a:b] = l[0]
+    return O, L

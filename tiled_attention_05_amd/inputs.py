@@ -73,6 +73,9 @@ WORKLOADS = {
                 mask=MASK_CAUSAL | MASK_DOC, softcap=50.0, alibi=True),
     5: Workload(5, "fp8_hadamard", B=4, Hq=16, Hkv=16, N=8192, d=128, dtype="fp8",
                 outlier_frac=0.001),
+    # packed variable-length batch: sequences of [128, 4096] tokens, causal within each
+    6: Workload(6, "varlen_causal_bf16", B=1, Hq=32, Hkv=8, N=32768, d=128, dtype="bf16",
+                mask=MASK_CAUSAL | MASK_DOC, extra={"varlen": True, "len_range": (128, 4096)}),
 }
 
 
@@ -126,11 +129,20 @@ def doc_ids(w: Workload, seed: int | None = None, aux=None):
     """int32 [B, N] non-decreasing document index per token (batch rows drawn in turn)."""
     rows = []
     g = aux_generator(w, seed) if aux is None else aux
+    lo, hi = w.extra.get("len_range", (512, 8192))
     for b in range(w.B):
-        lens = doc_lengths(w.N, g)
+        lens = doc_lengths(w.N, g, lo, hi)
         rows.append(torch.repeat_interleave(torch.arange(len(lens), dtype=torch.int32),
                                             torch.tensor(lens)))
     return torch.stack(rows)
+
+
+def cu_seqlens(ids_row):
+    """int32 [n + 1] start offsets of the runs of a non-decreasing id row
+    (the packed-sequence offsets of a variable-length batch), last = len."""
+    ids = torch.as_tensor(ids_row).to(torch.int64)
+    starts = torch.nonzero(torch.diff(ids, prepend=ids[:1] - 1)).flatten()
+    return torch.cat([starts, torch.tensor([ids.numel()])]).to(torch.int32)
 
 
 def alibi_slopes(H: int):
