@@ -97,6 +97,40 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              float softcap, const float* alibi_slopes, int dtype, void* stream);
 
 /*
+ * attn_fwd_varlen -- the same forward over a packed batch of variable-length
+ * sequences ("FlashAttention-3 : ...", section "Optimisations restantes et
+ * integration future": variable-length sequences). Sequence s owns tokens
+ * [cu_seqlens[s], cu_seqlens[s + 1]) of the packed dimension and attends only
+ * within itself: the document mask of "FlexAttention de PyTorch avec
+ * FlashAttention-4 change la donne" (opening section) over the concatenation.
+ *
+ * q, o       : [Hq][total][d]; k, v: [Hkv][total][d]; lse: float32 [Hq][total]
+ *              or NULL. Element types and O / LSE conventions as attn_fwd.
+ * cu_seqlens : device int32 [num_seqs + 1]: cu_seqlens[0] = 0, non-decreasing,
+ *              cu_seqlens[num_seqs] = total (empty sequences allowed). Tokens
+ *              past cu_seqlens[num_seqs] would form one more sequence: a
+ *              precondition violation, not detected (the offsets live on the
+ *              device).
+ * mask_kind  : ATTN_MASK_NONE, or ATTN_MASK_CAUSAL (j <= i within a sequence),
+ *              optionally | ATTN_MASK_WINDOW (with window W as in attn_fwd).
+ * softcap, alibi_slopes, scale, d, Hq, Hkv: as attn_fwd (ALiBi distances are
+ *              within a sequence).
+ * workspace  : device int32 [total], caller-owned; overwritten with each
+ *              token's sequence index before the forward runs (the library
+ *              allocates nothing). Must not alias another argument.
+ * dtype      : ATTN_F32 or ATTN_BF16.
+ * Errors     : ATTN_ERR_INVALID_ARG for NULL q/k/v/o/cu_seqlens/workspace,
+ *              num_seqs < 1, total < 1, mask bits other than CAUSAL / WINDOW,
+ *              and every attn_fwd argument error; ATTN_ERR_UNSUPPORTED for
+ *              ATTN_FP8_E4M3 and attn_fwd's unsupported cases. Every check runs
+ *              before the first HIP call.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int num_seqs, int total, int Hq, int Hkv, int d,
+                    float scale, int mask_kind, int window, float softcap,
+                    const float* alibi_slopes, int32_t* workspace, int dtype, void* stream);
+
+/*
  * fp8 incoherent-processing prepare step ("FlashAttention-3 : ...", section
  * "Basse precision FP8 et incoherent processing": Q and K are multiplied by a
  * Hadamard transform with random signs, per head, in O(d log d), to spread

@@ -87,6 +87,33 @@ def test_fwd_rejects_unsupported(lib, kw):
     assert _fwd(lib, **kw) == _lib.ERR_UNSUPPORTED
 
 
+def _varlen(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cu=FAKE, ns=3, total=100, Hq=2, Hkv=2, d=128, scale=0.1,
+             mask=1, window=0, softcap=0.0, slopes=None, ws=FAKE, dtype=1)
+    a.update(kw)
+    return lib.attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["ns"], a["total"], a["Hq"],
+                               a["Hkv"], a["d"], a["scale"], a["mask"], a["window"], a["softcap"], a["slopes"],
+                               a["ws"], a["dtype"], None)
+
+
+VARLEN_INVALID = [
+    dict(cu=None), dict(ws=None), dict(q=None), dict(o=None), dict(ns=0), dict(total=0),
+    dict(mask=4), dict(mask=5), dict(mask=8), dict(mask=3, window=0), dict(Hq=3, Hkv=2),
+    dict(scale=math.nan), dict(softcap=-2.0), dict(dtype=9),
+]
+VARLEN_UNSUPPORTED = [dict(dtype=2), dict(d=96), dict(mask=2, window=8)]
+
+
+@pytest.mark.parametrize("kw", VARLEN_INVALID)
+def test_fwd_varlen_rejects_invalid(lib, kw):
+    assert _varlen(lib, **kw) == _lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", VARLEN_UNSUPPORTED)
+def test_fwd_varlen_rejects_unsupported(lib, kw):
+    assert _varlen(lib, **kw) == _lib.ERR_UNSUPPORTED
+
+
 def test_fp8_buffer_bytes(lib):
     # 300 tokens -> 384 padded rows of 128 bytes, 3 float32 scales per head
     assert _lib.attn_fp8_buffer_bytes(2, 3, 300, 128) == 2 * 3 * 384 * 128 + 2 * 3 * 3 * 4

@@ -22,7 +22,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOC = 0, 1, 2, 4
 FP8_TILE = 128
 
-EXPORTS = ("attn_fwd", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_block_mask_bytes",
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_block_mask_bytes",
            "attn_block_mask_build", "attn_status_string")
 
 _lib = None
@@ -45,6 +45,9 @@ def load():
         lib.attn_fwd.restype = _i
         lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _f, _vp,
                                  _i, _vp]
+        lib.attn_fwd_varlen.restype = _i
+        lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _f, _vp,
+                                        _vp, _i, _vp]
         lib.attn_fp8_buffer_bytes.restype = _sz
         lib.attn_fp8_buffer_bytes.argtypes = [_i, _i, _i, _i]
         lib.attn_fp8_prepare.restype = _i
@@ -82,6 +85,13 @@ def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, window, d
     return load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, scale,
                            mask_kind, window, _ptr(doc_ids), softcap, _ptr(alibi_slopes), dtype,
                            _stream(stream))
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, total, Hq, Hkv, d, scale, mask_kind, window,
+                    softcap, alibi_slopes, workspace, dtype, stream=None) -> int:
+    return load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), num_seqs,
+                                  total, Hq, Hkv, d, scale, mask_kind, window, softcap, _ptr(alibi_slopes),
+                                  _ptr(workspace), dtype, _stream(stream))
 
 
 def attn_fp8_buffer_bytes(B, H, N, d) -> int:
@@ -138,6 +148,35 @@ def fwd(q, k, v, scale=None, mask=MASK_NONE, window=0, doc_ids=None, softcap=0.0
                   softcap, alibi_slopes, dt, stream)
     if st:
         raise AttnError(st, "attn_fwd")
+    return (o, lse) if with_lse else o
+
+
+def fwd_varlen(q, k, v, cu_seqlens, scale=None, mask=MASK_NONE, window=0, softcap=0.0, alibi_slopes=None,
+               with_lse=True, out=None, lse=None, workspace=None, stream=None):
+    """Forward over packed sequences: q [Hq, total, d], k / v [Hkv, total, d],
+    cu_seqlens int32 [num_seqs + 1] on the device (sequence s owns tokens
+    cu_seqlens[s] .. cu_seqlens[s + 1] - 1)."""
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(q.dtype)
+    if dt is None:
+        raise ValueError("q must be float32 or bfloat16")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, 3)
+    Hq, total, d = q.shape
+    Hkv = k.shape[0]
+    if v.shape != k.shape or k.shape[1] != total or k.shape[2] != d:
+        raise ValueError("k and v must be [Hkv, total, d] matching q")
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32, 1)
+    o = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty(Hq, total, device=q.device, dtype=torch.float32)
+    ws = torch.empty(total, device=q.device, dtype=torch.int32) if workspace is None else workspace
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = attn_fwd_varlen(q, k, v, o, lse if with_lse else None, cu_seqlens, cu_seqlens.numel() - 1, total, Hq,
+                         Hkv, d, sc, mask, window, softcap, alibi_slopes, ws, dt, stream)
+    if st:
+        raise AttnError(st, "attn_fwd_varlen")
     return (o, lse) if with_lse else o
 
 

@@ -19,6 +19,7 @@ hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B
                               int d, const int8_t* signs, void* q8, void* k8, void* v8, hipStream_t st);
 hipError_t launch_block_mask(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int bm,
                              int bn, void* out, hipStream_t st);
+hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* ids, hipStream_t st);
 }  // namespace attn
 
 namespace {
@@ -66,9 +67,14 @@ const char* attn_status_string(int status) {
     }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-             int Nq, int Nk, int d, float scale, int mask_kind, int window, const int32_t* doc_ids,
-             float softcap, const float* alibi_slopes, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of attn_fwd, with no HIP call.
+int fwd_check(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nq, int Nk,
+              int d, float scale, int mask_kind, int window, const int32_t* doc_ids, float softcap,
+              const float* alibi_slopes, int dtype) {
     if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
     if (Hq % Hkv) return ATTN_ERR_INVALID_ARG;
@@ -82,7 +88,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (dtype == ATTN_FP8_E4M3 &&
         (d != 128 || Nq != Nk || mask_kind != 0 || softcap != 0.f || alibi_slopes != nullptr))
         return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
 
+int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+               int Nq, int Nk, int d, float scale, int mask_kind, int window, const int32_t* doc_ids,
+               float softcap, const float* alibi_slopes, int dtype, void* stream) {
     attn::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
     p.doc = (mask_kind & ATTN_MASK_DOC) ? doc_ids : nullptr;
@@ -105,6 +116,39 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     else if (dtype == ATTN_F32) e = attn::launch_fwd_f32(p, d, st);
     else e = attn::launch_fwd_fp8(p, d, st);
     return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+             int Nq, int Nk, int d, float scale, int mask_kind, int window, const int32_t* doc_ids,
+             float softcap, const float* alibi_slopes, int dtype, void* stream) {
+    if (const int r = fwd_check(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, window, doc_ids, softcap,
+                                alibi_slopes, dtype))
+        return r;
+    return fwd_launch(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, window, doc_ids, softcap,
+                      alibi_slopes, dtype, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int num_seqs, int total, int Hq, int Hkv, int d, float scale,
+                    int mask_kind, int window, float softcap, const float* alibi_slopes, int32_t* workspace,
+                    int dtype, void* stream) {
+    if (!cu_seqlens || !workspace || num_seqs < 1 || total < 1) return ATTN_ERR_INVALID_ARG;
+    if (mask_kind & ~(ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW)) return ATTN_ERR_INVALID_ARG;
+    if (dtype == ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    const int mask = mask_kind | ATTN_MASK_DOC;
+    if (const int r = fwd_check(q, k, v, o, 1, Hq, Hkv, total, total, d, scale, mask, window, workspace,
+                                softcap, alibi_slopes, dtype))
+        return r;
+    if (log_enabled())
+        std::fprintf(stderr, "[attn] fwd_varlen num_seqs=%d total=%d\n", num_seqs, total);
+    if (const int r = hip_status(attn::launch_seq_ids(cu_seqlens, num_seqs, total, workspace, (hipStream_t)stream)))
+        return r;
+    return fwd_launch(q, k, v, o, lse, 1, Hq, Hkv, total, total, d, scale, mask, window, workspace, softcap,
+                      alibi_slopes, dtype, stream);
 }
 
 size_t attn_fp8_buffer_bytes(int B, int H, int N, int d) {
