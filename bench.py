@@ -41,7 +41,8 @@ KERNEL_SOURCES = {"bf16": ["attn_fwd_bf16.hip", "fwd_common.h", "common.h", "fwd
                   "fp8": ["fp8.hip", "fwd_common.h", "common.h", "fwd_params.h"],
                   "f32": ["attn_fwd_f32.hip", "fwd_common.h", "common.h", "fwd_params.h"]}
 PROFILE_SUMMARY = {2: "profiles/fwd_bf16_causal_prefill_b4_h32_n4096_d128.md",
-                   5: "profiles/fwd_fp8_dense_b4_h16_n8192_d128.md"}
+                   5: "profiles/fwd_fp8_dense_b4_h16_n8192_d128.md",
+                   6: "profiles/fwd_bf16_varlen_causal_t32768_h32x8_d128.md"}
 
 
 def sources_hash(kind):
@@ -119,7 +120,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -152,6 +153,16 @@ def main():
 
         def prep():
             _lib.fp8_prepare(q, k, v, dev["signs"])
+    elif w.extra.get("varlen"):
+        # packed sequences through attn_fwd_varlen: [H][total][d] views of the B = 1 tensors
+        cu = I.cu_seqlens(x["doc_ids"][0]).to("cuda")
+        ws = torch.empty(w.N, dtype=torch.int32, device="cuda")
+        o = torch.empty_like(q)
+        extra = {"sequences": int(cu.numel() - 1)}
+
+        def step():
+            _lib.fwd_varlen(q[0], k[0], v[0], cu, scale=w.scale, mask=w.mask & ~I.MASK_DOC, window=w.window,
+                            softcap=w.softcap, alibi_slopes=dev["slopes"], out=o[0], lse=lse[0], workspace=ws)
     else:
         o = torch.empty_like(q)
 
@@ -213,8 +224,10 @@ def main():
                      "peak_at_sclk": None if sclk is None else round(peak * sclk / PEAK_MHZ, 1),
                      "frac_at_sclk": None if sclk is None else round(achieved / (peak * sclk / PEAK_MHZ), 4)},
     }
-    if extra:
+    if extra and w.dtype == "fp8":
         out["fp8_prepare"] = extra
+    elif extra:
+        out["config"].update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
