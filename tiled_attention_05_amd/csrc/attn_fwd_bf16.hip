@@ -471,10 +471,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // Copies of tile i + PF may go out anywhere between barriers i and i + 1.
     // Issued by all waves right after the barrier they queue up behind each
     // other (the CU's vector-memory path drains about 64 bytes per cycle) and
-    // hold every wave; in the plain kernel (no modifier, no document ids)
-    // they go out at the end of the interval instead. (The other kernels run
-    // out of registers with the copies there.)
-    constexpr bool LATE_A = ATTN_LATE_COPY_A && !DOC && !MODS, LATE_B = ATTN_LATE_COPY_B && !DOC && !MODS;
+    // hold every wave; in the kernels without score modifiers they go out at
+    // the end of the interval instead. (The modifier kernels run out of
+    // registers with the copies there.)
+    constexpr bool LATE_A = ATTN_LATE_COPY_A && !MODS, LATE_B = ATTN_LATE_COPY_B && !MODS;
     // Iteration it over a tile of this wave's key range: softmax and GEMM1 of
     // tile it, GEMM0 of tile it + 1 (when it is also in the range).
     auto body = [&](int it, bool next) __attribute__((always_inline)) {
