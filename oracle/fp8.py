@@ -116,11 +116,40 @@ def dequantize_rows(codes, scales, tile=SCALE_TILE):
     return v * rep[..., None]
 
 
-def prepare(q, k, v, signs, tile=SCALE_TILE):
-    """The fp8 prepare step: rotate Q and K, then quantise Q, K, V per tile.
+def rope_tables(N, d, base=10000.0):
+    """cos / sin of the rotary angles t * base^(-2i/d), t < N, i < d/2, float64 [N, d/2]."""
+    t = np.arange(N, dtype=np.float64)[:, None]
+    theta = base ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+    return np.cos(t * theta), np.sin(t * theta)
+
+
+def rope(x, cos, sin):
+    """Rotary position embedding of x [..., N, d] with the given tables [N, d/2].
+
+    Dimension i (< d/2) is paired with i + d/2 and the pair is turned by the
+    token's angle: (a, b) -> (a cos - b sin, a sin + b cos). Applied to Q and K
+    before the Hadamard rotation: both are memory-bound passes over the same
+    rows, so one kernel can do both ("FlashAttention-3 : ...", section "Basse
+    precision FP8 et incoherent processing"). The pairing and the caller-given
+    tables are readings; the page names the rotary embedding only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    c = np.asarray(cos, dtype=np.float64)
+    s = np.asarray(sin, dtype=np.float64)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def prepare(q, k, v, signs, tile=SCALE_TILE, rope_cos=None, rope_sin=None):
+    """The fp8 prepare step: (optionally RoPE, then) rotate Q and K, then
+    quantise Q, K, V per tile.
 
     Returns dict with the rotated float64 inputs and the (codes, scales) triples.
     """
+    if rope_cos is not None:
+        q = rope(q, rope_cos, rope_sin)
+        k = rope(k, rope_cos, rope_sin)
     qr = rotate(q, signs)
     kr = rotate(k, signs)
     vv = np.asarray(v, dtype=np.float64)
