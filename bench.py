@@ -202,7 +202,19 @@ def main():
         torch.cuda.synchronize()
         ms_prep = e0.elapsed_time(e1) / 10
         prep_bytes = 2 * (q.numel() + k.numel() + v.numel()) + q8.numel() + k8.numel() + v8.numel()
+        # the same step with the rotary embedding of Q and K fused in front
+        rc, rs = (t.to("cuda") for t in I.rope_tables(w.N, w.d))
+        for _ in range(2):
+            _lib.fp8_prepare(q, k, v, dev["signs"], rope_cos=rc, rope_sin=rs)
+        e0.record()
+        for _ in range(10):
+            _lib.fp8_prepare(q, k, v, dev["signs"], rope_cos=rc, rope_sin=rs)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_rope = e0.elapsed_time(e1) / 10
+        rope_bytes = prep_bytes + 2 * rc.numel() * 4
         extra = {"prepare_ms": round(ms_prep, 4), "prepare_GBps": round(prep_bytes / ms_prep / 1e6, 1),
+                 "prepare_rope_ms": round(ms_rope, 4), "prepare_rope_GBps": round(rope_bytes / ms_rope / 1e6, 1),
                  "end_to_end_tflops": round(fl / ((ms_prep + ms_kernel) * 1e-3) / 1e12, 2)}
     traffic, sclk = measured_profile(args.workload, dt)
     out = {

@@ -160,6 +160,27 @@ int attn_fp8_prepare(const void* q, const void* k, const void* v,
                      void* q8, void* k8, void* v8, void* stream);
 
 /*
+ * attn_fp8_prepare_rope -- the same prepare step with the rotary position
+ * embedding of Q and K fused in front of the Hadamard rotation (same page and
+ * section: the Hadamard transform is memory-bound and can be fused with a
+ * preceding memory-bound step such as the rotary embedding at no extra cost).
+ * For token t and pair i < d/2, (x_i, x_{i+d/2}) becomes
+ *   (x_i * rope_cos[t][i] - x_{i+d/2} * rope_sin[t][i],
+ *    x_i * rope_sin[t][i] + x_{i+d/2} * rope_cos[t][i]);
+ * then signs, Hadamard and quantisation exactly as attn_fp8_prepare. V is
+ * neither turned nor rotated.
+ *
+ * rope_cos, rope_sin : device float32 [N][d/2], caller-owned (usually
+ *   cos / sin of t * base^(-2i/d)); token t of every batch row and head uses
+ *   row t. Errors: ATTN_ERR_INVALID_ARG for NULL tables, otherwise as
+ *   attn_fp8_prepare.
+ */
+int attn_fp8_prepare_rope(const void* q, const void* k, const void* v,
+                          int B, int Hq, int Hkv, int N, int d, const int8_t* signs,
+                          const float* rope_cos, const float* rope_sin,
+                          void* q8, void* k8, void* v8, void* stream);
+
+/*
  * Block mask builder ("FlexAttention de PyTorch ...", section "Limitations
  * actuelles": block sparsity).  Classifies every (query tile, key tile) pair of
  * a block_m x block_n tiling of the Nq x Nk score matrix of batch row b:

@@ -128,6 +128,19 @@ def test_fp8_prepare_validation(lib):
     assert f(FAKE, FAKE, FAKE, 1, 2, 2, 8, 64, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_UNSUPPORTED
 
 
+def test_fp8_prepare_rope_validation(lib):
+    f = lib.attn_fp8_prepare_rope
+    ok = (FAKE, FAKE, FAKE, 1, 2, 2, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    for i, want in ((9, _lib.ERR_INVALID_ARG), (10, _lib.ERR_INVALID_ARG), (0, _lib.ERR_INVALID_ARG),
+                    (11, _lib.ERR_INVALID_ARG)):
+        a = list(ok)
+        a[i] = None
+        assert f(*a) == want
+    a = list(ok)
+    a[7] = 64
+    assert f(*a) == _lib.ERR_UNSUPPORTED
+
+
 def test_block_mask_validation(lib):
     assert _lib.attn_block_mask_bytes(1, 100, 100, 0, 64) == 0
     assert _lib.attn_block_mask_bytes(1, 100, 100, 8192, 64) == 0

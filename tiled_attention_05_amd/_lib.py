@@ -22,8 +22,8 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOC = 0, 1, 2, 4
 FP8_TILE = 128
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_block_mask_bytes",
-           "attn_block_mask_build", "attn_status_string")
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_fp8_prepare_rope",
+           "attn_block_mask_bytes", "attn_block_mask_build", "attn_status_string")
 
 _lib = None
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -52,6 +52,9 @@ def load():
         lib.attn_fp8_buffer_bytes.argtypes = [_i, _i, _i, _i]
         lib.attn_fp8_prepare.restype = _i
         lib.attn_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]
+        lib.attn_fp8_prepare_rope.restype = _i
+        lib.attn_fp8_prepare_rope.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _vp]
         lib.attn_block_mask_bytes.restype = _sz
         lib.attn_block_mask_bytes.argtypes = [_i, _i, _i, _i, _i]
         lib.attn_block_mask_build.restype = _i
@@ -101,6 +104,11 @@ def attn_fp8_buffer_bytes(B, H, N, d) -> int:
 def attn_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8, stream=None) -> int:
     return load().attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, _ptr(signs), _ptr(q8),
                                    _ptr(k8), _ptr(v8), _stream(stream))
+
+
+def attn_fp8_prepare_rope(q, k, v, B, Hq, Hkv, N, d, signs, rope_cos, rope_sin, q8, k8, v8, stream=None) -> int:
+    return load().attn_fp8_prepare_rope(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, _ptr(signs), _ptr(rope_cos),
+                                        _ptr(rope_sin), _ptr(q8), _ptr(k8), _ptr(v8), _stream(stream))
 
 
 def attn_block_mask_bytes(B, Nq, Nk, block_m, block_n) -> int:
@@ -180,13 +188,21 @@ def fwd_varlen(q, k, v, cu_seqlens, scale=None, mask=MASK_NONE, window=0, softca
     return (o, lse) if with_lse else o
 
 
-def fp8_prepare(q, k, v, signs, stream=None):
+def fp8_prepare(q, k, v, signs, stream=None, rope_cos=None, rope_sin=None):
     """Rotate Q, K (random-sign Hadamard; none if signs is None) and quantise Q, K, V
-    to packed e4m3 buffers."""
+    to packed e4m3 buffers. With rope_cos / rope_sin (float32 [N, d/2]) the
+    rotary embedding of Q and K runs first, in the same kernel."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, 4)
     if signs is not None:
         _need(signs, "signs", torch.int8, 1)
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("rope_cos and rope_sin go together")
+    if rope_cos is not None:
+        _need(rope_cos, "rope_cos", torch.float32, 2)
+        _need(rope_sin, "rope_sin", torch.float32, 2)
+        if rope_cos.shape != (q.shape[2], q.shape[3] // 2) or rope_sin.shape != rope_cos.shape:
+            raise ValueError("rope tables must be [N, d/2]")
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     nq = attn_fp8_buffer_bytes(B, Hq, N, d)
@@ -194,7 +210,10 @@ def fp8_prepare(q, k, v, signs, stream=None):
     q8 = torch.empty(nq, dtype=torch.uint8, device=q.device)
     k8 = torch.empty(nk, dtype=torch.uint8, device=q.device)
     v8 = torch.empty(nk, dtype=torch.uint8, device=q.device)
-    st = attn_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8, stream)
+    if rope_cos is None:
+        st = attn_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8, stream)
+    else:
+        st = attn_fp8_prepare_rope(q, k, v, B, Hq, Hkv, N, d, signs, rope_cos, rope_sin, q8, k8, v8, stream)
     if st:
         raise AttnError(st, "attn_fp8_prepare")
     return q8, k8, v8

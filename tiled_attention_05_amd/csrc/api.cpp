@@ -16,7 +16,8 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t st);
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, hipStream_t st);
 hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N,
-                              int d, const int8_t* signs, void* q8, void* k8, void* v8, hipStream_t st);
+                              int d, const int8_t* signs, const float* rope_cos, const float* rope_sin, void* q8,
+                              void* k8, void* v8, hipStream_t st);
 hipError_t launch_block_mask(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int bm,
                              int bn, void* out, hipStream_t st);
 hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* ids, hipStream_t st);
@@ -164,7 +165,19 @@ int attn_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq,
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv) return ATTN_ERR_INVALID_ARG;
     if ((long long)B * Hq * N * d > kMaxElems) return ATTN_ERR_INVALID_ARG;
     if (d != 128) return ATTN_ERR_UNSUPPORTED;
-    return hip_status(attn::launch_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8,
+    return hip_status(attn::launch_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, nullptr, nullptr, q8, k8, v8,
+                                               (hipStream_t)stream));
+}
+
+int attn_fp8_prepare_rope(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N, int d,
+                          const int8_t* signs, const float* rope_cos, const float* rope_sin, void* q8, void* k8,
+                          void* v8, void* stream) {
+    if (!rope_cos || !rope_sin) return ATTN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !q8 || !k8 || !v8) return ATTN_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv) return ATTN_ERR_INVALID_ARG;
+    if ((long long)B * Hq * N * d > kMaxElems) return ATTN_ERR_INVALID_ARG;
+    if (d != 128) return ATTN_ERR_UNSUPPORTED;
+    return hip_status(attn::launch_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, rope_cos, rope_sin, q8, k8, v8,
                                                (hipStream_t)stream));
 }
 

@@ -29,10 +29,17 @@ constexpr float kFp8PShift = 4.f;    // P is stored as e4m3(p * 2^4 * s_v / s_vm
 // round-to-nearest-even e4m3 values of x / scale (clamped to +-448 first, so
 // nothing saturates to NaN). V is not rotated and is written transposed,
 // [d][tokens], so the attention kernel reads contiguous keys per lane.
+// With rotary tables (rope_cos / rope_sin, float32 [N][d/2]) Q and K rows are
+// first turned pairwise, (x_i, x_{i+d/2}) by the token's angle: both passes
+// are memory-bound over the same rows, so they share one read and one write
+// ("FlashAttention-3 : ...", section "Basse precision FP8 et incoherent
+// processing").
 __global__ __launch_bounds__(128) void fp8_prepare_kernel(const __bf16* __restrict__ q,
                                                           const __bf16* __restrict__ k,
                                                           const __bf16* __restrict__ v, int B, int Hq,
                                                           int Hkv, int N, int Np, const int8_t* __restrict__ signs,
+                                                          const float* __restrict__ rope_cos,
+                                                          const float* __restrict__ rope_sin,
                                                           uint8_t* __restrict__ q8, uint8_t* __restrict__ k8,
                                                           uint8_t* __restrict__ v8) {
     constexpr int D = 128;
@@ -63,6 +70,22 @@ __global__ __launch_bounds__(128) void fp8_prepare_kernel(const __bf16* __restri
     } else {
 #pragma unroll
         for (int d = 0; d < D; ++d) x[d] = 0.f;
+    }
+    if (which < 2 && rope_cos != nullptr && row < N) {
+        const float4* c4 = (const float4*)(rope_cos + (size_t)row * (D / 2));
+        const float4* s4 = (const float4*)(rope_sin + (size_t)row * (D / 2));
+#pragma unroll
+        for (int i4 = 0; i4 < D / 8; ++i4) {
+            const float4 c = c4[i4], sn = s4[i4];
+            const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e;
+                const float a = x[i], b2 = x[i + D / 2];
+                x[i] = __builtin_fmaf(a, cc[e], -b2 * ss[e]);
+                x[i + D / 2] = __builtin_fmaf(a, ss[e], b2 * cc[e]);
+            }
+        }
     }
     if (which < 2 && signs != nullptr) {
 #pragma unroll
@@ -123,15 +146,16 @@ __global__ __launch_bounds__(128) void fp8_prepare_kernel(const __bf16* __restri
 }
 
 hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N, int d,
-                              const int8_t* signs, void* q8, void* k8, void* v8, hipStream_t st) {
+                              const int8_t* signs, const float* rope_cos, const float* rope_sin, void* q8,
+                              void* k8, void* v8, hipStream_t st) {
     if (d != 128) return hipErrorNotSupported;
     const int Np = (N + kFp8Tile - 1) / kFp8Tile * kFp8Tile;
     const int nt = Np / kFp8Tile;
     const long long blocks = (long long)B * (Hq + 2 * Hkv) * nt;
     if (blocks > INT_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fp8_prepare_kernel, dim3((unsigned)blocks), dim3(128), 0, st, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, B, Hq, Hkv, N, Np, signs, (uint8_t*)q8, (uint8_t*)k8,
-                       (uint8_t*)v8);
+                       (const __bf16*)k, (const __bf16*)v, B, Hq, Hkv, N, Np, signs, rope_cos, rope_sin,
+                       (uint8_t*)q8, (uint8_t*)k8, (uint8_t*)v8);
     return hipGetLastError();
 }
 

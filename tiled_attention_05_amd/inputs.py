@@ -145,6 +145,13 @@ def cu_seqlens(ids_row):
     return torch.cat([starts, torch.tensor([ids.numel()])]).to(torch.int32)
 
 
+def rope_tables(N: int, d: int, base: float = 10000.0):
+    """float32 [N, d/2] cos and sin of the rotary angles t * base^(-2i/d) (computed in float64)."""
+    t = torch.arange(N, dtype=torch.float64)[:, None]
+    theta = base ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    return torch.cos(t * theta).to(torch.float32), torch.sin(t * theta).to(torch.float32)
+
+
 def alibi_slopes(H: int):
     """float32 [H]: 2^(-8 (h + 1) / H)."""
     h = torch.arange(H, dtype=torch.float64)
