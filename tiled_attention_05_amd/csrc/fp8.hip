@@ -22,19 +22,33 @@ constexpr float kE4m3Max = 448.f;
 constexpr float kFp8PShift = 4.f;    // P is stored as e4m3(p * 2^4 * s_v / s_vmax), p <= 2^4
 
 // -----------------------------------------------------------------------------
-// Prepare: one workgroup per (tensor, batch, head, 128-token tile), one thread
-// per token. Q and K rows: x <- (x * signs) H / sqrt(d) by an in-register fast
-// Walsh-Hadamard transform (Sylvester order, 7 butterfly stages for d = 128).
-// Then the tile's amax gives scale = amax / 448 and the codes are the
-// round-to-nearest-even e4m3 values of x / scale (clamped to +-448 first, so
-// nothing saturates to NaN). V is not rotated and is written transposed,
-// [d][tokens], so the attention kernel reads contiguous keys per lane.
+// Prepare: one workgroup (4 waves) per (tensor, batch, head, 128-token tile).
+// Lane layout: 4 lanes per token; lane c of a quad holds the 8-dim chunks
+// c, c + 4, c + 8, c + 12, i.e. dims 8c + 32j + e (j, e < 4, 8): every load
+// instruction reads 64 contiguous bytes of each of 16 token rows, and of the
+// 7 index bits of a dim, bits 0-2 (e) and 5-6 (j) are in the lane's registers
+// and bits 3-4 (c) across the quad. A wave covers 16 tokens per step, the 4
+// waves 64, two steps the tile. Q and K rows: x <- (x * signs) H / sqrt(d),
+// the Walsh-Hadamard transform in Sylvester order: butterflies on bits 0-2 and
+// 5-6 in registers, on bits 3-4 with quad permutes (xor 1, xor 2); butterflies
+// on different bits commute, so their order does not change the result. Then
+// the tile's amax gives scale = amax / 448 and the codes are the round-to-
+// nearest-even e4m3 values of x / scale (clamped to +-448 first, so nothing
+// saturates to NaN). V is not rotated and is written transposed, [d][tokens],
+// so the attention kernel reads contiguous keys per lane.
 // With rotary tables (rope_cos / rope_sin, float32 [N][d/2]) Q and K rows are
-// first turned pairwise, (x_i, x_{i+d/2}) by the token's angle: both passes
-// are memory-bound over the same rows, so they share one read and one write
-// ("FlashAttention-3 : ...", section "Basse precision FP8 et incoherent
-// processing").
-__global__ __launch_bounds__(128) void fp8_prepare_kernel(const __bf16* __restrict__ q,
+// first turned pairwise, (x_i, x_{i+d/2}) by the token's angle (the pair sits
+// in one lane: j and j + 2): both passes are memory-bound over the same rows,
+// so they share one read and one write ("FlashAttention-3 : ...", section
+// "Basse precision FP8 et incoherent processing").
+__device__ __forceinline__ float quad_xor(float v, int m) {
+    // DPP quad permutes: xor 1 = [1, 0, 3, 2] (0xB1), xor 2 = [2, 3, 0, 1] (0x4E)
+    const int i = __float_as_int(v);
+    return __int_as_float(m == 1 ? __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true)
+                                 : __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));
+}
+
+__global__ __launch_bounds__(256) void fp8_prepare_kernel(const __bf16* __restrict__ q,
                                                           const __bf16* __restrict__ k,
                                                           const __bf16* __restrict__ v, int B, int Hq,
                                                           int Hkv, int N, int Np, const int8_t* __restrict__ signs,
@@ -42,8 +56,8 @@ __global__ __launch_bounds__(128) void fp8_prepare_kernel(const __bf16* __restri
                                                           const float* __restrict__ rope_sin,
                                                           uint8_t* __restrict__ q8, uint8_t* __restrict__ k8,
                                                           uint8_t* __restrict__ v8) {
-    constexpr int D = 128;
-    __shared__ float red[2];
+    constexpr int D = 128, STEPS = kFp8Tile / 64;   // 64 tokens per step over the 4 waves
+    __shared__ float red[4];
     __shared__ __attribute__((aligned(16))) uint8_t vt[D][kFp8Tile];
     const int nt = Np / kFp8Tile;
     const int nq = B * Hq * nt, nk = B * Hkv * nt;
@@ -55,93 +69,154 @@ __global__ __launch_bounds__(128) void fp8_prepare_kernel(const __bf16* __restri
     else if (id < nq + nk) { which = 1; id -= nq; src = k; dst = k8; H = Hkv; }
     else { which = 2; id -= nq + nk; src = v; dst = v8; H = Hkv; }
     const int tile = id % nt, bh = id / nt;
-    const int t = threadIdx.x;
-    const int row = tile * kFp8Tile + t;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane & 3;              // quad lane: chunks c + 4 j
+    const int tq = lane >> 2;            // token of the wave's 16
+    const bool rot = which < 2 && signs != nullptr;
+    const bool rope = which < 2 && rope_cos != nullptr;
 
-    float x[D];
-    if (row < N) {
-        const bf16x8* s8 = (const bf16x8*)(src + ((size_t)bh * N + row) * D);
+    float sg[4][8];
+    if (rot) {
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const bf16x8 w = s8[c];
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[8 * c + e] = (float)w[e];
-        }
-    } else {
-#pragma unroll
-        for (int d = 0; d < D; ++d) x[d] = 0.f;
-    }
-    if (which < 2 && rope_cos != nullptr && row < N) {
-        const float4* c4 = (const float4*)(rope_cos + (size_t)row * (D / 2));
-        const float4* s4 = (const float4*)(rope_sin + (size_t)row * (D / 2));
-#pragma unroll
-        for (int i4 = 0; i4 < D / 8; ++i4) {
-            const float4 c = c4[i4], sn = s4[i4];
-            const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * i4 + e;
-                const float a = x[i], b2 = x[i + D / 2];
-                x[i] = __builtin_fmaf(a, cc[e], -b2 * ss[e]);
-                x[i + D / 2] = __builtin_fmaf(a, ss[e], b2 * cc[e]);
-            }
-        }
-    }
-    if (which < 2 && signs != nullptr) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) x[d] = signs[d] < 0 ? -x[d] : x[d];
-#pragma unroll
-        for (int len = 1; len < D; len <<= 1)
-#pragma unroll
-            for (int i = 0; i < D; i += 2 * len)
-#pragma unroll
-                for (int j = i; j < i + len; ++j) {
-                    const float a = x[j], b2 = x[j + len];
-                    x[j] = a + b2;
-                    x[j + len] = a - b2;
-                }
-        const float r = 0.08838834764831845f;   // 1 / sqrt(128)
-#pragma unroll
-        for (int d = 0; d < D; ++d) x[d] *= r;
+            for (int e = 0; e < 8; ++e) sg[j][e] = signs[8 * c + 32 * j + e] < 0 ? -1.f : 1.f;
     }
 
+    float x[STEPS][4][8];   // [step][j][e]: dim 8c + 32j + e
     float am = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) am = fmaxf(am, fabsf(x[d]));
+    for (int it = 0; it < STEPS; ++it) {
+        const int t = it * 64 + wave * 16 + tq;   // token within the tile
+        const int row = tile * kFp8Tile + t;
+        float (*y)[8] = x[it];
+        if (row < N) {
+            const __bf16* rp = src + ((size_t)bh * N + row) * D + 8 * c;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
-    if ((t & 63) == 0) red[t >> 6] = am;
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 w = *(const bf16x8*)(rp + 32 * j);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[j][e] = (float)w[e];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[j][e] = 0.f;
+        }
+        if (rope && row < N) {
+            // pair (i, i + 64) = (j, j + 2) of this lane, i = 8c + 32j + e, j < 2
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float4* c4 = (const float4*)(rope_cos + (size_t)row * (D / 2) + 8 * c + 32 * j);
+                const float4* s4 = (const float4*)(rope_sin + (size_t)row * (D / 2) + 8 * c + 32 * j);
+                const float4 c0 = c4[0], c1 = c4[1], s0 = s4[0], s1 = s4[1];
+                const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float a0 = y[j][e], b0 = y[j + 2][e];
+                    y[j][e] = __builtin_fmaf(a0, cs[e], -b0 * sn[e]);
+                    y[j + 2][e] = __builtin_fmaf(a0, sn[e], b0 * cs[e]);
+                }
+            }
+        }
+        if (rot) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[j][e] *= sg[j][e];
+            // index bits 0-2 (e) and 5-6 (j): in registers
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int len = 1; len < 8; len <<= 1)
+#pragma unroll
+                    for (int i = 0; i < 8; i += 2 * len)
+#pragma unroll
+                        for (int e = i; e < i + len; ++e) {
+                            const float a0 = y[j][e], b0 = y[j][e + len];
+                            y[j][e] = a0 + b0;
+                            y[j][e + len] = a0 - b0;
+                        }
+#pragma unroll
+            for (int lj = 1; lj < 4; lj <<= 1)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if ((j & lj) == 0)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float a0 = y[j][e], b0 = y[j + lj][e];
+                            y[j][e] = a0 + b0;
+                            y[j + lj][e] = a0 - b0;
+                        }
+            // index bits 3-4 (c): across the quad
+#pragma unroll
+            for (int m = 1; m < 4; m <<= 1) {
+                const bool upper = (c & m) != 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float p = quad_xor(y[j][e], m);
+                        y[j][e] = upper ? p - y[j][e] : y[j][e] + p;
+                    }
+            }
+            const float r = 0.08838834764831845f;   // 1 / sqrt(128)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[j][e] *= r;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[j][e]));
+    }
+#pragma unroll
+    for (int s2 = 32; s2 >= 1; s2 >>= 1) am = fmaxf(am, __shfl_xor(am, s2));
+    if (lane == 0) red[wave] = am;
     __syncthreads();
-    am = fmaxf(red[0], red[1]);
+    am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = am > 0.f ? am / kE4m3Max : 1.f;
     const float inv = 1.f / sc;
     float* scales = (float*)(dst + (size_t)B * H * Np * D);
-    if (t == 0) scales[(size_t)bh * nt + tile] = sc;
+    if (threadIdx.x == 0) scales[(size_t)bh * nt + tile] = sc;
 
-    uint32_t w[D / 4];
 #pragma unroll
-    for (int d = 0; d < D; d += 4) {
-        const float a0 = fminf(fmaxf(x[d] * inv, -kE4m3Max), kE4m3Max);
-        const float a1 = fminf(fmaxf(x[d + 1] * inv, -kE4m3Max), kE4m3Max);
-        const float a2 = fminf(fmaxf(x[d + 2] * inv, -kE4m3Max), kE4m3Max);
-        const float a3 = fminf(fmaxf(x[d + 3] * inv, -kE4m3Max), kE4m3Max);
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, pk, true);
-        w[d / 4] = (uint32_t)pk;
+    for (int it = 0; it < STEPS; ++it) {
+        const int t = it * 64 + wave * 16 + tq;
+        const int row = tile * kFp8Tile + t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t w2[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const float* z = x[it][j] + 4 * h2;
+                const float a0 = fminf(fmaxf(z[0] * inv, -kE4m3Max), kE4m3Max);
+                const float a1 = fminf(fmaxf(z[1] * inv, -kE4m3Max), kE4m3Max);
+                const float a2 = fminf(fmaxf(z[2] * inv, -kE4m3Max), kE4m3Max);
+                const float a3 = fminf(fmaxf(z[3] * inv, -kE4m3Max), kE4m3Max);
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, pk, true);
+                w2[h2] = (uint32_t)pk;
+            }
+            if (which < 2) {
+                *(uint2*)(dst + ((size_t)bh * Np + row) * D + 8 * c + 32 * j) = make_uint2(w2[0], w2[1]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vt[8 * c + 32 * j + e][t] = (uint8_t)(w2[e >> 2] >> (8 * (e & 3)));
+            }
+        }
     }
-    if (which < 2) {
-        uint4* o = (uint4*)(dst + ((size_t)bh * Np + row) * D);
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) o[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
-    } else {
-#pragma unroll
-        for (int d = 0; d < D; ++d) vt[d][t] = (uint8_t)(w[d >> 2] >> (8 * (d & 3)));
+    if (which == 2) {
         __syncthreads();
-        // thread t stores d-row t of the transposed tile: 128 consecutive tokens
-        const uint4* src4 = (const uint4*)&vt[t][0];
-        uint4* o = (uint4*)(dst + ((size_t)bh * D + t) * Np + (size_t)tile * kFp8Tile);
+        // thread i stores half (i & 1) of d-row i / 2 of the transposed tile
+        const int dr = threadIdx.x >> 1, half = threadIdx.x & 1;
+        const uint4* src4 = (const uint4*)&vt[dr][64 * half];
+        uint4* o = (uint4*)(dst + ((size_t)bh * D + dr) * Np + (size_t)tile * kFp8Tile + 64 * half);
 #pragma unroll
-        for (int c = 0; c < kFp8Tile / 16; ++c) o[c] = src4[c];
+        for (int i = 0; i < 4; ++i) o[i] = src4[i];
     }
 }
 
@@ -153,7 +228,7 @@ hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B
     const int nt = Np / kFp8Tile;
     const long long blocks = (long long)B * (Hq + 2 * Hkv) * nt;
     if (blocks > INT_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fp8_prepare_kernel, dim3((unsigned)blocks), dim3(128), 0, st, (const __bf16*)q,
+    hipLaunchKernelGGL(fp8_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, B, Hq, Hkv, N, Np, signs, rope_cos, rope_sin,
                        (uint8_t*)q8, (uint8_t*)k8, (uint8_t*)v8);
     return hipGetLastError();
