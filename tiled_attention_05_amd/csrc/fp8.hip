@@ -153,14 +153,11 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(const __bf16* __restri
             // index bits 3-4 (c): across the quad
 #pragma unroll
             for (int m = 1; m < 4; m <<= 1) {
-                const bool upper = (c & m) != 0;
+                const float sgn = (c & m) ? -1.f : 1.f;   // upper lane of the pair: partner - self
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float p = quad_xor(y[j][e], m);
-                        y[j][e] = upper ? p - y[j][e] : y[j][e] + p;
-                    }
+                    for (int e = 0; e < 8; ++e) y[j][e] = __builtin_fmaf(sgn, y[j][e], quad_xor(y[j][e], m));
             }
             const float r = 0.08838834764831845f;   // 1 / sqrt(128)
 #pragma unroll
