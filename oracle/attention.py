@@ -252,3 +252,36 @@ def attention_varlen(q, k, v, cu_seqlens, scale, mask_kind=MASK_NONE, window=0, 
         O[:, a:b] = o[0]
         L[:, a:b] = l[0]
     return O, L
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, block_size=16):
+    """Exact one-token decode over a paged key/value cache.
+
+    q [B, Hq, d] (the newest token of each sequence); k_cache / v_cache
+    [num_blocks, Hkv, block_size, d]; block_table [B, max_blocks] (logical block
+    i of sequence b lives in physical block block_table[b, i]); seq_lens [B].
+    The keys of sequence b are gathered in logical order and the query attends
+    to all of them ("Les kernels d'attention rapide ...", section "Attention de
+    type FlashAttention et attention paginee": the cache is kept in fixed-size
+    blocks addressed through a table). Returns (O [B, Hq, d], LSE [B, Hq]).
+    """
+    qn = np.asarray(_f64(q))
+    kc = _f64(k_cache)
+    vc = _f64(v_cache)
+    bt = np.asarray(block_table, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    B, Hq, d = qn.shape
+    O = np.zeros((B, Hq, d))
+    L = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(lens[b])
+        if n <= 0:
+            continue
+        nb = -(-n // block_size)
+        blocks = bt[b, :nb]
+        k = np.concatenate([kc[p] for p in blocks], axis=1)[:, :n]   # [Hkv, n, d]
+        v = np.concatenate([vc[p] for p in blocks], axis=1)[:, :n]
+        o, l = attention(qn[b][None, :, None, :], k[None], v[None], scale, threads=1)
+        O[b] = o[0, :, 0]
+        L[b] = l[0, :, 0]
+    return O, L
