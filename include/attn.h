@@ -197,6 +197,41 @@ int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window,
                           const int32_t* doc_ids, int block_m, int block_n,
                           void* out, void* stream);
 
+/*
+ * attn_decode_paged -- one new token per sequence attending to its whole
+ * key/value cache, stored in fixed-size blocks addressed through a block table
+ * ("Les kernels d'attention rapide et la fusion d'operateurs accelerent les
+ * modeles d'IA", section "Attention de type FlashAttention et attention
+ * paginee": the kernel translates every logical position through the table).
+ * Computes, per sequence b and query head h (grouped as in attn_fwd),
+ *   O[b][h] = softmax_j(scale * q[b][h] . k_j) v_j,  LSE[b][h] = log sum_j exp(...)
+ * over the seq_lens[b] keys of sequence b (no mask: the new token is the last
+ * position). The keys are split into num_splits ranges computed independently
+ * and merged exactly: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ *
+ * q          : bfloat16 [B][Hq][d]; o: bfloat16 [B][Hq][d]; lse: float32 [B][Hq]
+ *              or NULL (a sequence of length 0 gets O = 0, LSE = -inf).
+ * k_cache, v_cache : bfloat16 [num_blocks][Hkv][block_size][d]; token i of
+ *              sequence b is row i % block_size of physical block
+ *              block_table[b][i / block_size].
+ * block_table: device int32 [B][max_blocks]; seq_lens: device int32 [B], each in
+ *              [0, max_blocks * block_size]; the entries used must name valid
+ *              blocks (device data: a precondition, not checked).
+ * num_splits : 1..256; with more than one, workspace is device float32 of
+ *              attn_decode_workspace_floats(B, Hq, d, num_splits) entries
+ *              (caller-owned scratch, overwritten); NULL is allowed with 1.
+ * Supported  : dtype ATTN_BF16, d = 128, block_size = 16, Hq / Hkv <= 32.
+ * Errors     : ATTN_ERR_INVALID_ARG for NULL q/k_cache/v_cache/block_table/
+ *              seq_lens/o, sizes < 1, Hq % Hkv != 0, non-finite scale,
+ *              num_splits outside 1..256, a missing workspace, unknown dtype;
+ *              ATTN_ERR_UNSUPPORTED otherwise outside the supported set.
+ */
+size_t attn_decode_workspace_floats(int B, int Hq, int d, int num_splits);
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      int B, int Hq, int Hkv, int d, int block_size, int max_blocks, float scale,
+                      int num_splits, float* workspace, int dtype, void* stream);
+
 /* Static, human-readable text for an attn_status value (never NULL). */
 const char* attn_status_string(int status);
 

@@ -23,7 +23,8 @@ MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOC = 0, 1, 2, 4
 FP8_TILE = 128
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_fp8_prepare_rope",
-           "attn_block_mask_bytes", "attn_block_mask_build", "attn_status_string")
+           "attn_block_mask_bytes", "attn_block_mask_build", "attn_decode_workspace_floats", "attn_decode_paged",
+           "attn_status_string")
 
 _lib = None
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -55,6 +56,11 @@ def load():
         lib.attn_fp8_prepare_rope.restype = _i
         lib.attn_fp8_prepare_rope.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _vp]
+        lib.attn_decode_workspace_floats.restype = _sz
+        lib.attn_decode_workspace_floats.argtypes = [_i, _i, _i, _i]
+        lib.attn_decode_paged.restype = _i
+        lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
+                                          _i, _vp]
         lib.attn_block_mask_bytes.restype = _sz
         lib.attn_block_mask_bytes.argtypes = [_i, _i, _i, _i, _i]
         lib.attn_block_mask_build.restype = _i
@@ -109,6 +115,17 @@ def attn_fp8_prepare(q, k, v, B, Hq, Hkv, N, d, signs, q8, k8, v8, stream=None) 
 def attn_fp8_prepare_rope(q, k, v, B, Hq, Hkv, N, d, signs, rope_cos, rope_sin, q8, k8, v8, stream=None) -> int:
     return load().attn_fp8_prepare_rope(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, _ptr(signs), _ptr(rope_cos),
                                         _ptr(rope_sin), _ptr(q8), _ptr(k8), _ptr(v8), _stream(stream))
+
+
+def attn_decode_workspace_floats(B, Hq, d, num_splits) -> int:
+    return load().attn_decode_workspace_floats(B, Hq, d, num_splits)
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv, d, block_size, max_blocks,
+                      scale, num_splits, workspace, dtype, stream=None) -> int:
+    return load().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(o), _ptr(lse), B, Hq, Hkv, d, block_size, max_blocks, scale, num_splits,
+                                    _ptr(workspace), dtype, _stream(stream))
 
 
 def attn_block_mask_bytes(B, Nq, Nk, block_m, block_n) -> int:
@@ -185,6 +202,34 @@ def fwd_varlen(q, k, v, cu_seqlens, scale=None, mask=MASK_NONE, window=0, softca
                          Hkv, d, sc, mask, window, softcap, alibi_slopes, ws, dt, stream)
     if st:
         raise AttnError(st, "attn_fwd_varlen")
+    return (o, lse) if with_lse else o
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, num_splits=1, with_lse=True, out=None,
+                 lse=None, workspace=None, stream=None):
+    """One-token decode over a paged cache: q [B, Hq, d]; caches [num_blocks, Hkv, block_size, d];
+    block_table int32 [B, max_blocks]; seq_lens int32 [B] (device tensors)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, d = q.shape
+    _, Hkv, bs, _ = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_cache.shape[3] != d:
+        raise ValueError("caches must be [num_blocks, Hkv, block_size, d] matching q")
+    o = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    n = attn_decode_workspace_floats(B, Hq, d, num_splits)
+    ws = workspace
+    if ws is None and n > 0:
+        ws = torch.empty(n, device=q.device, dtype=torch.float32)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse if with_lse else None, B, Hq, Hkv,
+                           d, bs, block_table.shape[1], sc, num_splits, ws, BF16, stream)
+    if st:
+        raise AttnError(st, "attn_decode_paged")
     return (o, lse) if with_lse else o
 
 

@@ -21,6 +21,9 @@ hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B
 hipError_t launch_block_mask(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int bm,
                              int bn, void* out, hipStream_t st);
 hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* ids, hipStream_t st);
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* table, const int32_t* lens,
+                         void* o, float* lse, int B, int Hq, int Hkv, int max_blocks, float scale, int splits,
+                         float* workspace, hipStream_t st);
 }  // namespace attn
 
 namespace {
@@ -199,6 +202,29 @@ int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window, cons
                                               (mask_kind & ATTN_MASK_WINDOW) ? window : 0,
                                               (mask_kind & ATTN_MASK_DOC) ? doc_ids : nullptr, block_m,
                                               block_n, out, (hipStream_t)stream));
+}
+
+size_t attn_decode_workspace_floats(int B, int Hq, int d, int num_splits) {
+    if (B < 1 || Hq < 1 || d < 1 || num_splits < 1) return 0;
+    if (num_splits == 1) return 0;
+    return (size_t)B * Hq * num_splits * (d + 1);
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d, int block_size,
+                      int max_blocks, float scale, int num_splits, float* workspace, int dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || block_size < 1 || max_blocks < 1) return ATTN_ERR_INVALID_ARG;
+    if (Hq % Hkv || !std::isfinite(scale) || num_splits < 1 || num_splits > 256) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
+    if (num_splits > 1 && !workspace) return ATTN_ERR_INVALID_ARG;
+    if ((long long)B * Hq * num_splits > (1LL << 31) / 256) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_BF16 || d != 128 || block_size != 16 || Hq / Hkv > 32) return ATTN_ERR_UNSUPPORTED;
+    if (log_enabled())
+        std::fprintf(stderr, "[attn] decode_paged B=%d Hq=%d Hkv=%d max_blocks=%d splits=%d\n", B, Hq, Hkv,
+                     max_blocks, num_splits);
+    return hip_status(attn::launch_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv,
+                                          max_blocks, scale, num_splits, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

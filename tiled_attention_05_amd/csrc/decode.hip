@@ -1,0 +1,238 @@
+// One-token decode over a paged key/value cache, split over the keys.
+//
+// "Les kernels d'attention rapide et la fusion d'operateurs accelerent les
+// modeles d'IA", section "Attention de type FlashAttention et attention
+// paginee": the cache is stored in fixed-size blocks and a block table maps
+// each logical position to its physical block; the attention kernel
+// translates every position through the table. The keys of a sequence are
+// split into ranges processed independently; each range returns its
+// normalised output and its log-sum-exp, and the exact merge is
+// LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+//
+// Work: one wave per (sequence, key/value head, split). The G = Hq / Hkv query
+// heads of the group play the role of the query rows of the prefill kernel
+// (padded to 32): S^T = K Q^T on 32x32x16 bf16 products (a lane owns one head
+// and 16 of the 32 keys of a chunk), the same online softmax, O^T += V^T P^T
+// with V read transposed from LDS. K fragments are gathered straight into
+// registers through the table; V rows are gathered into a per-wave LDS tile by
+// direct global->LDS copies (per-lane addresses). The next chunk's loads are in
+// flight while the current chunk is computed. Decode reads every key once:
+// the kernel is bound by HBM, not by the padded products.
+#include <climits>
+
+#include "fwd_common.h"
+
+namespace attn {
+
+struct DecodeParams {
+    const __bf16* q;         // [B][Hq][128]
+    const __bf16* kc;        // [num_blocks][Hkv][16][128]
+    const __bf16* vc;
+    const int32_t* table;    // [B][max_blocks]
+    const int32_t* lens;     // [B]
+    __bf16* o;               // [B][Hq][128]
+    float* lse;              // [B][Hq] or null
+    float* part;             // splits > 1: [B][Hq][splits][128] outputs, then [B][Hq][splits] LSEs
+    int B, Hq, Hkv, G, max_blocks, splits;
+    float scale_log2;
+};
+
+constexpr int kPage = 16, kDD = 128, kCh = 32;   // page size, head dim, keys per chunk
+constexpr float kDecNoMax = -1e30f;              // initial reference: finite, below any score
+
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+    using T = Tile<kDD>;
+    constexpr int RB = T::ROW_BYTES;   // 256
+    __shared__ __attribute__((aligned(1024))) char vt_lds[4][2][kCh * RB];   // per wave, double-buffered
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wid = blockIdx.x * 4 + wave;
+    if (wid >= p.B * p.Hkv * p.splits) return;   // whole waves; the kernel has no barrier
+    const int split = wid % p.splits;
+    const int kvh = (wid / p.splits) % p.Hkv;
+    const int b = wid / (p.splits * p.Hkv);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int L = p.lens[b];
+    const int nch = (L + kCh - 1) / kCh;
+    const int cps = (nch + p.splits - 1) / p.splits;
+    const int c0 = min(split * cps, nch), c1 = min(c0 + cps, nch);
+    const int32_t* table = p.table + (size_t)b * p.max_blocks;
+    const size_t head_off = (size_t)kvh * kPage * kDD;
+    const size_t block_elems = (size_t)p.Hkv * kPage * kDD;
+
+    // Q fragments (B operand): lane holds head kvh G + l32 (zero beyond G), dims 16 s + 8 hh + 0..7
+    const bool qv = l32 < p.G;
+    const int h = kvh * p.G + (qv ? l32 : 0);
+    bf16x8 qf[8];
+    {
+        const __bf16* qr = p.q + ((size_t)b * p.Hq + h) * kDD + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = qv ? *(const bf16x8*)(qr + 16 * s) : bf16x8{};
+    }
+    // row of key `key` (clamped into the sequence) in a cache
+    auto row_of = [&](const __bf16* cache, int key) __attribute__((always_inline)) {
+        const int kk = min(key, L - 1);
+        return cache + (size_t)table[kk / kPage] * block_elems + head_off + (size_t)(kk % kPage) * kDD;
+    };
+    // V transposed reads (as the prefill kernel, one 32-key block): lane L of a
+    // 16-lane group addresses row 4 hh + L / 4 (+ 16 u, + 8 for the high half),
+    // columns 32 t + 16 cg + 4 (L % 4)
+    int vofs[4];
+    {
+        const int Ln = lane & 15, cg = (lane >> 4) & 1;
+        const int r = 4 * hh + (Ln >> 2);
+        const int col = 16 * cg + 4 * (Ln & 3);
+        const int v0 = r * RB + ((((col * 2) >> 4) ^ T::swz_v(r)) << 4) + ((col * 2) & 15);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vofs[t] = v0 ^ (64 * t);
+    }
+
+    bf16x8 kf[8];
+    auto load_k = [&](int c) __attribute__((always_inline)) {
+        const __bf16* kr = row_of(p.kc, c * kCh + l32) + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) kf[s] = *(const bf16x8*)(kr + 16 * s);
+    };
+    // V tile of chunk c into buffer c & 1: slot i 64 + lane = (row, 16-byte chunk), swizzled like the prefill tile
+    auto load_v = [&](int c) __attribute__((always_inline)) {
+        const unsigned base = lds_addr((ATTN_LDS char*)vt_lds[wave][c & 1]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int slot = i * 64 + lane, r = slot >> 4, pc = slot & 15;
+            const __bf16* src = row_of(p.vc, c * kCh + r) + 8 * (pc ^ T::swz_v(r));
+            dma16(src, base + i * 1024);
+        }
+    };
+
+    f32x16 o[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = f32x16{};
+    float m = kDecNoMax, l = 0.f;
+
+    if (c0 < c1) {
+        load_k(c0);
+        load_v(c0);
+    }
+    for (int c = c0; c < c1; ++c) {
+        // this chunk's K registers and V tile have landed; then the next chunk's loads go out
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) s = mfma_bf16(kf[st], qf[st], s);
+        if (c + 1 < c1) {
+            load_k(c + 1);
+            load_v(c + 1);
+        }
+        const int kv0 = c * kCh;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            s[r] = key < L ? s[r] * p.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, s[r]);
+        }
+        mx = xhalf_max(mx);
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        float ls = 0.f;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(s[r] - m);
+            ls += pr;
+            pf[r >> 3][r & 7] = (__bf16)pr;
+        }
+        l = l * alpha + ls;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] *= alpha;
+        const ATTN_LDS char* vb = (const ATTN_LDS char*)vt_lds[wave][c & 1];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const ATTN_LDS char* a = vb + vofs[t] + 16 * u * RB;
+                const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)a);
+                const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)(a + 8 * RB));
+                o[t] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pf[u], o[t]);
+            }
+        // the next iteration refills the other buffer only after its own wait,
+        // by which time these reads have returned
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+
+    const float lt = xhalf_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_v = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    if (!qv) return;
+    const size_t bh = (size_t)b * p.Hq + h;
+    if (p.splits == 1) {
+        __bf16* orow = p.o + bh * kDD + 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                bf16x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[t][4 * gq + e] * inv);
+                *(bf16x4*)(orow + 32 * t + 8 * gq) = w;
+            }
+        if (p.lse && hh == 0) p.lse[bh] = lse_v;
+    } else {
+        float* po = p.part + (bh * p.splits + split) * kDD + 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = o[t][4 * gq + e] * inv;
+                *(f32x4*)(po + 32 * t + 8 * gq) = w;
+            }
+        if (hh == 0) p.part[(size_t)p.B * p.Hq * p.splits * kDD + bh * p.splits + split] = lse_v;
+    }
+}
+
+// Exact merge of the splits: one workgroup per (sequence, head), thread = dim.
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
+    const size_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const float* ls = p.part + (size_t)p.B * p.Hq * p.splits * kDD + bh * p.splits;
+    float mx = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, ls[s]);
+    float acc = 0.f, den = 0.f;
+    if (mx > -INFINITY) {
+        for (int s = 0; s < p.splits; ++s) {
+            const float w = __expf(ls[s] - mx);   // 0 for an empty split (LSE = -inf)
+            den += w;
+            acc += w * p.part[(bh * p.splits + s) * kDD + d];
+        }
+    }
+    p.o[bh * kDD + d] = (__bf16)(den > 0.f ? acc / den : 0.f);
+    if (p.lse && d == 0) p.lse[bh] = den > 0.f ? mx + __logf(den) : -INFINITY;
+}
+
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* table, const int32_t* lens,
+                         void* o, float* lse, int B, int Hq, int Hkv, int max_blocks, float scale, int splits,
+                         float* workspace, hipStream_t st) {
+    DecodeParams p{};
+    p.q = (const __bf16*)q;
+    p.kc = (const __bf16*)kc;
+    p.vc = (const __bf16*)vc;
+    p.table = table;
+    p.lens = lens;
+    p.o = (__bf16*)o;
+    p.lse = lse;
+    p.part = workspace;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.max_blocks = max_blocks; p.splits = splits;
+    p.scale_log2 = scale * kLog2e;
+    const long long waves = (long long)B * Hkv * splits;
+    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * Hq)), dim3(128), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -73,6 +73,9 @@ WORKLOADS = {
                 mask=MASK_CAUSAL | MASK_DOC, softcap=50.0, alibi=True),
     5: Workload(5, "fp8_hadamard", B=4, Hq=16, Hkv=16, N=8192, d=128, dtype="fp8",
                 outlier_frac=0.001),
+    # one-token decode over a paged cache: 64 sequences of [1024, 8192] cached tokens, 16-token blocks
+    7: Workload(7, "decode_paged_bf16", B=64, Hq=32, Hkv=8, N=8192, d=128, dtype="bf16",
+                extra={"decode": True, "len_range": (1024, 8192), "block": 16}),
     # packed variable-length batch: sequences of [128, 4096] tokens, causal within each
     6: Workload(6, "varlen_causal_bf16", B=1, Hq=32, Hkv=8, N=32768, d=128, dtype="bf16",
                 mask=MASK_CAUSAL | MASK_DOC, extra={"varlen": True, "len_range": (128, 4096)}),
@@ -135,6 +138,34 @@ def doc_ids(w: Workload, seed: int | None = None, aux=None):
         rows.append(torch.repeat_interleave(torch.arange(len(lens), dtype=torch.int32),
                                             torch.tensor(lens)))
     return torch.stack(rows)
+
+
+def decode_inputs(B, Hq, Hkv, d, lens, block=16, seed=0, dtype=torch.bfloat16):
+    """Paged decode inputs: q [B, Hq, d]; k_cache / v_cache [num_blocks, Hkv, block, d]
+    holding every sequence's keys in blocks placed by a seeded permutation;
+    block_table int32 [B, max_blocks] (unused entries 0); seq_lens int32 [B]."""
+    g = torch.Generator("cpu").manual_seed(1000 + seed)
+    lens = [int(x) for x in lens]
+    nbs = [-(-n // block) for n in lens]
+    total = max(1, sum(nbs))
+    maxb = max(1, max(nbs))
+    q = torch.randn(B, Hq, d, generator=g).to(dtype)
+    kc = torch.randn(total, Hkv, block, d, generator=g).to(dtype)
+    vc = torch.randn(total, Hkv, block, d, generator=g).to(dtype)
+    perm = torch.randperm(total, generator=g)
+    table = torch.zeros(B, maxb, dtype=torch.int32)
+    at = 0
+    for b, nb in enumerate(nbs):
+        table[b, :nb] = perm[at:at + nb].to(torch.int32)
+        at += nb
+    return q, kc, vc, table, torch.tensor(lens, dtype=torch.int32)
+
+
+def decode_lengths(w: Workload, seed: int | None = None):
+    """Cached lengths of a decode workload: uniform on its len_range, from the auxiliary generator."""
+    lo, hi = w.extra["len_range"]
+    g = aux_generator(w, seed)
+    return torch.randint(lo, hi + 1, (w.B,), generator=g).tolist()
 
 
 def cu_seqlens(ids_row):
