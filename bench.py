@@ -38,11 +38,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tiled_attention_05_amd", "csrc")
 # kernel sources whose hash keys the measured HBM traffic of a profile summary
 KERNEL_SOURCES = {"bf16": ["attn_fwd_bf16.hip", "fwd_common.h", "common.h", "fwd_params.h"],
+                  "decode": ["decode.hip", "fwd_common.h", "common.h"],
                   "fp8": ["fp8.hip", "fwd_common.h", "common.h", "fwd_params.h"],
                   "f32": ["attn_fwd_f32.hip", "fwd_common.h", "common.h", "fwd_params.h"]}
 PROFILE_SUMMARY = {2: "profiles/fwd_bf16_causal_prefill_b4_h32_n4096_d128.md",
                    5: "profiles/fwd_fp8_dense_b4_h16_n8192_d128.md",
-                   6: "profiles/fwd_bf16_varlen_causal_t32768_h32x8_d128.md"}
+                   6: "profiles/fwd_bf16_varlen_causal_t32768_h32x8_d128.md",
+                   7: "profiles/decode_paged_b64_h32x8_d128_len1k-8k.md"}
 
 
 def sources_hash(kind):
@@ -115,12 +117,62 @@ def run_cpu_baseline(w, x, budget_s=15.0):
                      "pool_threads": threads, "blas_threads_per_job": 1}}
 
 
+def bench_decode(w, args):
+    """Paged decode (attn_decode_paged): HBM-bound, measured in GB/s of algorithmic bytes --
+    every cached key and value row of every sequence read once, Q read and O written once."""
+    lens = I.decode_lengths(w)
+    q, kc, vc, bt, sl = (t.to("cuda") for t in I.decode_inputs(w.B, w.Hq, w.Hkv, w.d, lens, w.extra["block"],
+                                                                 seed=w.k))
+    splits = w.extra.get("splits", 4)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, device="cuda", dtype=torch.float32)
+    ws = torch.empty(_lib.attn_decode_workspace_floats(w.B, w.Hq, w.d, splits), device="cuda",
+                     dtype=torch.float32)
+
+    def step():
+        _lib.decode_paged(q, kc, vc, bt, sl, scale=w.scale, num_splits=splits, out=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_kernel = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    n_keys = sum(lens)
+    nbytes = n_keys * w.Hkv * 2 * w.d * 2 + 2 * q.numel() * 2 + lse.numel() * 4 + sl.numel() * 4 + \
+        sum(-(-n // w.extra["block"]) for n in lens) * 4
+    fl = 4 * w.d * n_keys * w.Hq
+    gbps = nbytes / (ms_kernel * 1e-3) / 1e9
+    traffic, sclk = measured_profile(args.workload, "decode")
+    out = {
+        "metric": "paged decode HBM bandwidth (algorithmic bytes)", "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "block": w.extra["block"],
+                   "cached_tokens": n_keys, "len_min": min(lens), "len_max": max(lens), "splits": splits,
+                   "bytes_per_step": nbytes, "flops_per_step": fl, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbps / 8000.0, 4), "traffic": traffic, "kernel_ms": round(ms_kernel, 4),
+                     "kernel_ms_median": round(per_launch[len(per_launch) // 2], 4),
+                     "kernel_ms_min": round(per_launch[0], 4), "tflops": round(fl / (ms_kernel * 1e-3) / 1e12, 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -138,6 +190,9 @@ def main():
     _lib.load()
 
     w = I.WORKLOADS[args.workload]
+    if w.extra.get("decode"):
+        bench_decode(w, args)
+        return
     x = I.inputs(w)
     dev = {k: (None if v is None else v.to("cuda").contiguous()) for k, v in x.items()}
     q, k, v = dev["q"], dev["k"], dev["v"]
