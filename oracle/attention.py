@@ -285,3 +285,43 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, block_size=1
         O[b] = o[0, :, 0]
         L[b] = l[0, :, 0]
     return O, L
+
+
+def attention_backward(q, k, v, do, scale, mask_kind=MASK_NONE):
+    """Exact gradients of the forward (float64) for an output gradient ``do``.
+
+    With P the row softmax of the masked scores s = scale q.k, O = P V and
+    D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij):
+        dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
+    summed over the query heads of each key/value head. This is the chain rule
+    through the softmax; the method recomputes P from the saved LSE instead of
+    storing it, and its result stays exact and deterministic ("FlashAttention-2
+    (FR)", section "Performance et efficacite"). q [B,Hq,N,d], k/v [B,Hkv,Nk,d],
+    do like q. Returns (dQ, dK, dV) float64.
+    """
+    q, k, v, do = (np.asarray(_f64(x)) for x in (q, k, v, do))
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    G = Hq // Hkv
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    ok = allowed_mask(np.arange(Nq), np.arange(Nk), Nq, Nk, mask_kind)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = scale * q[b, h] @ k[b, g].T
+            s = np.where(ok, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            m = np.where(np.isfinite(m), m, 0.0)
+            e = np.where(ok, np.exp(s - m), 0.0)
+            l = e.sum(axis=1, keepdims=True)
+            P = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)
+            O = P @ v[b, g]
+            dP = do[b, h] @ v[b, g].T
+            D = (do[b, h] * O).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dQ[b, h] = scale * dS @ k[b, g]
+            dK[b, g] += scale * dS.T @ q[b, h]
+            dV[b, g] += P.T @ do[b, h]
+    return dQ, dK, dV
