@@ -232,6 +232,30 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int B, int Hq, int Hkv, int d, int block_size, int max_blocks, float scale,
                       int num_splits, float* workspace, int dtype, void* stream);
 
+/*
+ * attn_bwd -- gradients of attn_fwd (no modifiers) for an output gradient dO.
+ * With P_ij = exp(scale q_i . k_j - LSE_i) recomputed from the forward's LSE
+ * and D_i = sum_c dO_ic O_ic:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
+ * dK and dV summed over the query heads of each key/value head. Exact and
+ * deterministic ("FlashAttention-2 (FR)", section "Performance et efficacite";
+ * "FlexAttention de PyTorch avec FlashAttention-4 change la donne", section
+ * "Limitations actuelles", names the non-deterministic backward this avoids):
+ * no gradient is accumulated with atomics.
+ *
+ * q, o, dout, dq : bfloat16 [B][Hq][N][d]; k, v, dk, dv: bfloat16 [B][Hkv][N][d];
+ * lse        : float32 [B][Hq][N], the forward's natural-log LSE of the same call.
+ * workspace  : device float32 [B][Hq][N], caller-owned scratch (D), overwritten.
+ * mask_kind  : ATTN_MASK_NONE or ATTN_MASK_CAUSAL (Nq = Nk = N).
+ * Supported  : dtype ATTN_BF16, d = 128. Errors: ATTN_ERR_INVALID_ARG for a NULL
+ *              pointer, sizes < 1, Hq % Hkv != 0, non-finite scale, unknown mask
+ *              bits or dtype; ATTN_ERR_UNSUPPORTED for other dtypes, d != 128,
+ *              WINDOW or DOC masks.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* workspace,
+             int B, int Hq, int Hkv, int N, int d, float scale, int mask_kind, int dtype, void* stream);
+
 /* Static, human-readable text for an attn_status value (never NULL). */
 const char* attn_status_string(int status);
 

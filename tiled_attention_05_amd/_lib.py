@@ -24,7 +24,7 @@ FP8_TILE = 128
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_fp8_prepare_rope",
            "attn_block_mask_bytes", "attn_block_mask_build", "attn_decode_workspace_floats", "attn_decode_paged",
-           "attn_status_string")
+           "attn_bwd", "attn_status_string")
 
 _lib = None
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -61,6 +61,8 @@ def load():
         lib.attn_decode_paged.restype = _i
         lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
                                           _i, _vp]
+        lib.attn_bwd.restype = _i
+        lib.attn_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp]
         lib.attn_block_mask_bytes.restype = _sz
         lib.attn_block_mask_bytes.argtypes = [_i, _i, _i, _i, _i]
         lib.attn_block_mask_build.restype = _i
@@ -126,6 +128,12 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq,
     return load().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                     _ptr(o), _ptr(lse), B, Hq, Hkv, d, block_size, max_blocks, scale, num_splits,
                                     _ptr(workspace), dtype, _stream(stream))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, mask_kind, dtype,
+             stream=None) -> int:
+    return load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(workspace), B, Hq, Hkv, N, d, scale, mask_kind, dtype, _stream(stream))
 
 
 def attn_block_mask_bytes(B, Nq, Nk, block_m, block_n) -> int:
@@ -203,6 +211,22 @@ def fwd_varlen(q, k, v, cu_seqlens, scale=None, mask=MASK_NONE, window=0, softca
     if st:
         raise AttnError(st, "attn_fwd_varlen")
     return (o, lse) if with_lse else o
+
+
+def bwd(q, k, v, o, dout, lse, scale=None, mask=MASK_NONE, workspace=None, stream=None):
+    """(dQ, dK, dV) of the forward for output gradient dout (bf16 BHSD, d = 128)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(B * Hq * N, device=q.device, dtype=torch.float32) if workspace is None else workspace
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, Hq, Hkv, N, d, sc, mask, BF16, stream)
+    if st:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, num_splits=1, with_lse=True, out=None,

@@ -24,6 +24,9 @@ hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* i
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* table, const int32_t* lens,
                          void* o, float* lse, int B, int Hq, int Hkv, int max_blocks, float scale, int splits,
                          float* workspace, hipStream_t st);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, float scale,
+                      int causal, hipStream_t st);
 }  // namespace attn
 
 namespace {
@@ -225,6 +228,22 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, c
                      max_blocks, num_splits);
     return hip_status(attn::launch_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv,
                                           max_blocks, scale, num_splits, workspace, (hipStream_t)stream));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, int d, float scale,
+             int mask_kind, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (mask_kind & ~kKnownMask) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
+    if ((long long)B * Hq * N * d > kMaxElems) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_BF16 || d != 128 || (mask_kind & ~ATTN_MASK_CAUSAL)) return ATTN_ERR_UNSUPPORTED;
+    if (log_enabled())
+        std::fprintf(stderr, "[attn] bwd B=%d Hq=%d Hkv=%d N=%d mask=%d\n", B, Hq, Hkv, N, mask_kind);
+    return hip_status(attn::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, scale,
+                                       mask_kind & ATTN_MASK_CAUSAL, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,259 @@
+// Attention backward: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
+//
+// With P_ij = exp(scale q_i.k_j - LSE_i) recomputed from the saved LSE (the
+// N x N matrix is never stored) and D_i = sum_c dO_ic O_ic:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+// The result is exact and deterministic ("FlashAttention-2 (FR)", section
+// "Performance et efficacite"); FlexAttention's backward loses determinism with
+// block sparsity ("FlexAttention de PyTorch avec FlashAttention-4 change la
+// donne", section "Limitations actuelles") -- here no gradient is accumulated
+// with atomics: dK / dV are owned by one wave per key block (looping over the
+// queries and the group's query heads), dQ by one wave per query block.
+//
+// Products are 32x32x16 bf16 MFMAs (A: lane l holds row l % 32, k = 8 (l / 32)
+// + 0..7; B: column l % 32; C: lane l, register r holds row 8 (r / 4) +
+// 4 (l / 32) + r % 4, column l % 32). Operands read row-wise come straight from
+// global memory; operands needed transposed (Q^T, dO^T, K^T) go through a
+// per-wave LDS tile in the prefill kernel's swizzled layout and its transposed
+// reads, and the probabilities are packed in the matching permuted order.
+#include <climits>
+
+#include "fwd_common.h"
+
+namespace attn {
+
+struct BwdParams {
+    const __bf16 *q, *k, *v, *o, *dout;   // BHSD bf16
+    const float* lse;                     // [B][Hq][N] natural log
+    float* dsum;                          // [B][Hq][N] scratch: D_i
+    __bf16 *dq, *dk, *dv;
+    int B, Hq, Hkv, G, N;
+    float scale, scale_log2;
+    int causal;
+};
+
+constexpr int kBD = 128, kBC = 32;   // head dim, rows per block / chunk
+
+// D_i = sum_c dO_ic O_ic (float32), one wave per 64 rows: lane = row.
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdParams p) {
+    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t rows = (size_t)p.B * p.Hq * p.N;
+    if (row >= rows) return;
+    const bf16x8* a = (const bf16x8*)(p.dout + row * kBD);
+    const bf16x8* b = (const bf16x8*)(p.o + row * kBD);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kBD / 8; ++c) {
+        const bf16x8 x = a[c], y = b[c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
+    }
+    p.dsum[row] = s;
+}
+
+// Transposed-read offsets of the prefill kernel (one 32-row tile): lane L of a
+// 16-lane group addresses row 4 hh + L / 4 (+ 16 u, + 8 for the high half),
+// columns 32 t + 16 cg + 4 (L % 4).
+__device__ __forceinline__ void tr_offsets(int lane, int ofs[4]) {
+    using T = Tile<kBD>;
+    const int hh = lane >> 5, Ln = lane & 15, cg = (lane >> 4) & 1;
+    const int r = 4 * hh + (Ln >> 2);
+    const int col = 16 * cg + 4 * (Ln & 3);
+    const int v0 = r * T::ROW_BYTES + ((((col * 2) >> 4) ^ T::swz_v(r)) << 4) + ((col * 2) & 15);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ofs[t] = v0 ^ (64 * t);
+}
+
+// Rows r0 .. r0 + 31 of one head (row-major [N][128], rows clamped to N - 1)
+// into a per-wave LDS tile, swizzled for the transposed reads.
+__device__ __forceinline__ void tile_to_lds(const __bf16* head, int r0, int N, unsigned base, int lane) {
+    using T = Tile<kBD>;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int slot = i * 64 + lane, r = slot >> 4, pc = slot & 15;
+        const __bf16* src = head + (size_t)min(r0 + r, N - 1) * kBD + 8 * (pc ^ T::swz_v(r));
+        dma16(src, base + i * 1024);
+    }
+}
+
+// A-operand (or B-operand) fragments of rows r0 + l32: dims 16 s + 8 hh + 0..7.
+__device__ __forceinline__ void row_frags(const __bf16* head, int r0, int N, int lane, bf16x8 f[8]) {
+    const __bf16* rp = head + (size_t)min(r0 + (lane & 31), N - 1) * kBD + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = *(const bf16x8*)(rp + 16 * s);
+}
+
+// Product of a tile read transposed from LDS (A: 32 d-rows x 16 tile rows, per
+// output tile t and step u) with packed values (B): acc[t] += A_t,u B_u.
+__device__ __forceinline__ void tr_gemm(const ATTN_LDS char* tile, const int ofs[4], const bf16x8 pk[2],
+                                        f32x16 acc[4]) {
+    constexpr int RB = Tile<kBD>::ROW_BYTES;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const ATTN_LDS char* a = tile + ofs[t] + 16 * u * RB;
+            const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)a);
+            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)(a + 8 * RB));
+            acc[t] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pk[u], acc[t]);
+        }
+}
+
+// Writes acc (C layout: rows = d, column = lane's row r0 + l32) scaled by f as
+// bf16 rows of [N][128].
+__device__ __forceinline__ void store_rows(__bf16* head, int r0, int N, int lane, const f32x16 acc[4], float f) {
+    const int row = r0 + (lane & 31);
+    if (row >= N) return;
+    __bf16* orow = head + (size_t)row * kBD + 4 * (lane >> 5);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[t][4 * gq + e] * f);
+            *(bf16x4*)(orow + 32 * t + 8 * gq) = w;
+        }
+}
+
+// dK, dV: one wave per (batch, key/value head, 32-key block).
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[4][2][kBC * Tile<kBD>::ROW_BYTES];   // per wave: Q, dO
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nkb = (p.N + kBC - 1) / kBC;
+    const int wid = blockIdx.x * 4 + wave;
+    if (wid >= p.B * p.Hkv * nkb) return;   // whole waves; no barrier in this kernel
+    const int kb = wid % nkb, g = (wid / nkb) % p.Hkv, b = wid / (nkb * p.Hkv);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int j0 = kb * kBC;
+    const size_t kvh = ((size_t)b * p.Hkv + g) * p.N * kBD;
+    bf16x8 kf[8], vf[8];
+    row_frags(p.k + kvh, j0, p.N, lane, kf);   // B operand of S = Q K^T: column = key
+    row_frags(p.v + kvh, j0, p.N, lane, vf);   // B operand of dP = dO V^T
+    int ofs[4];
+    tr_offsets(lane, ofs);
+    const unsigned qt = lds_addr((ATTN_LDS char*)lds[wave][0]), dt = lds_addr((ATTN_LDS char*)lds[wave][1]);
+    f32x16 dv[4], dk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dv[t] = dk[t] = f32x16{};
+    const int key = j0 + l32;
+    const int qc0 = p.causal ? kb : 0;   // the first query chunk that sees the block
+    const int nqc = (p.N + kBC - 1) / kBC;
+    for (int hi = 0; hi < p.G; ++hi) {
+        const int h = g * p.G + hi;
+        const size_t qh = ((size_t)b * p.Hq + h) * p.N;
+        for (int qc = qc0; qc < nqc; ++qc) {
+            const int i0 = qc * kBC;
+            tile_to_lds(p.q + qh * kBD, i0, p.N, qt, lane);
+            tile_to_lds(p.dout + qh * kBD, i0, p.N, dt, lane);
+            bf16x8 af[8];
+            // S = Q K^T and dP = dO V^T: lane = key, registers = queries 8 (r / 4) + 4 hh + r % 4
+            row_frags(p.q + qh * kBD, i0, p.N, lane, af);
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int st = 0; st < 8; ++st) s = mfma_bf16(af[st], kf[st], s);
+            row_frags(p.dout + qh * kBD, i0, p.N, lane, af);
+            f32x16 dp = f32x16{};
+#pragma unroll
+            for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], vf[st], dp);
+            bf16x8 pk[2], sk[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qrow = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int qc = min(qrow, p.N - 1);
+                const bool ok = qrow < p.N && key < p.N && (!p.causal || key <= qrow);
+                const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - p.lse[qh + qc] * kLog2e) : 0.f;
+                pk[r >> 3][r & 7] = (__bf16)pr;
+                sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - p.dsum[qh + qc]));
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the Q and dO tiles are in LDS
+            tr_gemm((const ATTN_LDS char*)lds[wave][1], ofs, pk, dv);   // dV^T += dO^T P
+            tr_gemm((const ATTN_LDS char*)lds[wave][0], ofs, sk, dk);   // dK^T += Q^T dS
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next refill
+        }
+    }
+    store_rows(p.dk + kvh, j0, p.N, lane, dk, p.scale);
+    store_rows(p.dv + kvh, j0, p.N, lane, dv, 1.f);
+}
+
+// dQ: one wave per (batch, query head, 32-query block).
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[4][kBC * Tile<kBD>::ROW_BYTES];   // per wave: K
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nqb = (p.N + kBC - 1) / kBC;
+    const int wid = blockIdx.x * 4 + wave;
+    if (wid >= p.B * p.Hq * nqb) return;
+    const int qb = wid % nqb, h = (wid / nqb) % p.Hq, b = wid / (nqb * p.Hq);
+    const int g = h / p.G;
+    const int l32 = lane & 31;
+    const int i0 = qb * kBC;
+    const size_t qh = ((size_t)b * p.Hq + h) * p.N;
+    const size_t kvh = ((size_t)b * p.Hkv + g) * p.N * kBD;
+    bf16x8 qf[8], df[8];
+    row_frags(p.q + qh * kBD, i0, p.N, lane, qf);      // B operand of S^T = K Q^T: column = query
+    row_frags(p.dout + qh * kBD, i0, p.N, lane, df);   // B operand of dP^T = V dO^T
+    const int qrow = i0 + l32;
+    const float lse2 = p.lse[qh + min(qrow, p.N - 1)] * kLog2e;
+    const float dd = p.dsum[qh + min(qrow, p.N - 1)];
+    int ofs[4];
+    tr_offsets(lane, ofs);
+    const unsigned kt = lds_addr((ATTN_LDS char*)lds[wave]);
+    f32x16 dq[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dq[t] = f32x16{};
+    const int hh = lane >> 5;
+    const int nkc = p.causal ? min(qb + 1, (p.N + kBC - 1) / kBC) : (p.N + kBC - 1) / kBC;
+    for (int kc = 0; kc < nkc; ++kc) {
+        const int j0 = kc * kBC;
+        tile_to_lds(p.k + kvh, j0, p.N, kt, lane);
+        bf16x8 af[8];
+        // S^T = K Q^T, dP^T = V dO^T: lane = query, registers = keys 8 (r / 4) + 4 hh + r % 4
+        row_frags(p.k + kvh, j0, p.N, lane, af);
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) s = mfma_bf16(af[st], qf[st], s);
+        row_frags(p.v + kvh, j0, p.N, lane, af);
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], df[st], dp);
+        bf16x8 sk[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = qrow < p.N && key < p.N && (!p.causal || key <= qrow);
+            const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - lse2) : 0.f;
+            sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dd));
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the K tile is in LDS
+        tr_gemm((const ATTN_LDS char*)lds[wave], ofs, sk, dq);   // dQ^T += K^T dS^T
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    store_rows(p.dq + qh * kBD, i0, p.N, lane, dq, p.scale);
+}
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, float scale,
+                      int causal, hipStream_t st) {
+    BwdParams p{};
+    p.q = (const __bf16*)q; p.k = (const __bf16*)k; p.v = (const __bf16*)v;
+    p.o = (const __bf16*)o; p.dout = (const __bf16*)dout;
+    p.lse = lse; p.dsum = workspace;
+    p.dq = (__bf16*)dq; p.dk = (__bf16*)dk; p.dv = (__bf16*)dv;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.N = N;
+    p.scale = scale; p.scale_log2 = scale * kLog2e; p.causal = causal;
+    const size_t rows = (size_t)p.B * p.Hq * p.N;
+    hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long nb = (p.N + kBC - 1) / kBC;
+    const long long w1 = (long long)p.B * p.Hkv * nb, w2 = (long long)p.B * p.Hq * nb;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn
