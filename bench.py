@@ -167,12 +167,57 @@ def bench_decode(w, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_backward(w, args):
+    """attn_bwd after one forward of the same inputs; FLOPs: 2.5x the forward's mask-adjusted
+    count (the five products of the gradient: S, dP, dV, dK, dQ; the kernels recompute S and dP
+    once more for dQ, which is not counted)."""
+    x = I.inputs(w)
+    g = torch.Generator("cpu").manual_seed(2000 + w.k)
+    q, k, v = (x[n].to("cuda") for n in ("q", "k", "v"))
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).to("cuda")
+    o, lse = _lib.fwd(q, k, v, scale=w.scale, mask=w.mask)
+    ws = torch.empty(w.B * w.Hq * w.N, device="cuda", dtype=torch.float32)
+    fl = 2.5 * flops.attention_flops(w.B, w.Hq, w.N, w.N, w.d, w.mask, w.window, None)
+
+    def step():
+        _lib.bwd(q, k, v, o, do, lse, scale=w.scale, mask=w.mask, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_kernel = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    achieved = fl / (ms_kernel * 1e-3) / 1e12
+    out = {
+        "metric": "attention bwd TFLOPS (2.5x the mask-adjusted forward FLOPs)",
+        "value": round(fl / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "mask": mask_name(w.mask), "flops_per_step": fl, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": None,
+                     "kernel_ms": round(ms_kernel, 4), "kernel_ms_median": round(per_launch[len(per_launch) // 2], 4),
+                     "kernel_ms_min": round(per_launch[0], 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--calibrate-copy", action="store_true", help="only run a 1 GiB device copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -192,6 +237,9 @@ def main():
     w = I.WORKLOADS[args.workload]
     if w.extra.get("decode"):
         bench_decode(w, args)
+        return
+    if w.extra.get("backward"):
+        bench_backward(w, args)
         return
     x = I.inputs(w)
     dev = {k: (None if v is None else v.to("cuda").contiguous()) for k, v in x.items()}

@@ -73,6 +73,9 @@ WORKLOADS = {
                 mask=MASK_CAUSAL | MASK_DOC, softcap=50.0, alibi=True),
     5: Workload(5, "fp8_hadamard", B=4, Hq=16, Hkv=16, N=8192, d=128, dtype="fp8",
                 outlier_frac=0.001),
+    # backward of the causal prefill (same shapes as workload 2)
+    8: Workload(8, "causal_prefill_bf16_backward", B=4, Hq=32, Hkv=32, N=4096, d=128, dtype="bf16",
+                mask=MASK_CAUSAL, extra={"backward": True}),
     # one-token decode over a paged cache: 64 sequences of [1024, 8192] cached tokens, 16-token blocks
     7: Workload(7, "decode_paged_bf16", B=64, Hq=32, Hkv=8, N=8192, d=128, dtype="bf16",
                 extra={"decode": True, "len_range": (1024, 8192), "block": 16, "splits": 16}),
