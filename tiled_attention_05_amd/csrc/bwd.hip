@@ -83,6 +83,16 @@ __device__ __forceinline__ void row_frags(const __bf16* head, int r0, int N, int
     for (int s = 0; s < 8; ++s) f[s] = *(const bf16x8*)(rp + 16 * s);
 }
 
+// Row fragments (A or B operand: row l32 of the tile, dims 16 s + 8 hh + 0..7)
+// read from an LDS tile in the swizzled layout of tile_to_lds.
+__device__ __forceinline__ void lds_row_frags(const ATTN_LDS char* tile, int lane, bf16x8 f[8]) {
+    using T = Tile<kBD>;
+    const int r = lane & 31, hh = lane >> 5;
+    const ATTN_LDS char* rp = tile + r * T::ROW_BYTES;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = *(const ATTN_LDS bf16x8*)(rp + (((2 * s + hh) ^ T::swz_v(r)) << 4));
+}
+
 // Product of a tile read transposed from LDS (A: 32 d-rows x 16 tile rows, per
 // output tile t and step u) with packed values (B): acc[t] += A_t,u B_u.
 __device__ __forceinline__ void tr_gemm(const ATTN_LDS char* tile, const int ofs[4], const bf16x8 pk[2],
@@ -116,9 +126,14 @@ __device__ __forceinline__ void store_rows(__bf16* head, int r0, int N, int lane
         }
 }
 
-// dK, dV: one wave per (batch, key/value head, 32-key block).
+// dK, dV: one wave per (batch, key/value head, 32-key block), looping over
+// the query chunks of every query head of the group. The next chunk's Q / dO
+// tiles and statistics are requested before the current chunk is computed (two
+// LDS buffer sets, unrolled by two); Q and dO fragments are read from them, so
+// the loop has no load the compiler counts.
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[4][2][kBC * Tile<kBD>::ROW_BYTES];   // per wave: Q, dO
+    __shared__ __attribute__((aligned(1024))) char lds[4][2][2][kBC * Tile<kBD>::ROW_BYTES];   // wave, buffer, Q / dO
+    __shared__ __attribute__((aligned(16))) float stat[4][2][2 * kBC];   // wave, buffer: LSE then D of the chunk
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nkb = (p.N + kBC - 1) / kBC;
@@ -131,55 +146,79 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     bf16x8 kf[8], vf[8];
     row_frags(p.k + kvh, j0, p.N, lane, kf);   // B operand of S = Q K^T: column = key
     row_frags(p.v + kvh, j0, p.N, lane, vf);   // B operand of dP = dO V^T
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no compiler-counted load stays pending into the loop
     int ofs[4];
     tr_offsets(lane, ofs);
-    const unsigned qt = lds_addr((ATTN_LDS char*)lds[wave][0]), dt = lds_addr((ATTN_LDS char*)lds[wave][1]);
     f32x16 dv[4], dk[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dv[t] = dk[t] = f32x16{};
     const int key = j0 + l32;
     const int qc0 = p.causal ? kb : 0;   // the first query chunk that sees the block
     const int nqc = (p.N + kBC - 1) / kBC;
-    for (int hi = 0; hi < p.G; ++hi) {
-        const int h = g * p.G + hi;
-        const size_t qh = ((size_t)b * p.Hq + h) * p.N;
-        for (int qc = qc0; qc < nqc; ++qc) {
-            const int i0 = qc * kBC;
-            tile_to_lds(p.q + qh * kBD, i0, p.N, qt, lane);
-            tile_to_lds(p.dout + qh * kBD, i0, p.N, dt, lane);
-            bf16x8 af[8];
-            // S = Q K^T and dP = dO V^T: lane = key, registers = queries 8 (r / 4) + 4 hh + r % 4
-            row_frags(p.q + qh * kBD, i0, p.N, lane, af);
-            f32x16 s = f32x16{};
+    const int per_head = nqc - qc0, total = p.G * per_head;
+
+    auto issue = [&](int it, int buf) __attribute__((always_inline)) {
+        const int h = g * p.G + it / per_head, i0 = (qc0 + it % per_head) * kBC;
+        const size_t qh = ((size_t)b * p.Hq + h) * p.N * kBD;
+        tile_to_lds(p.q + qh, i0, p.N, lds_addr((ATTN_LDS char*)lds[wave][buf][0]), lane);
+        tile_to_lds(p.dout + qh, i0, p.N, lds_addr((ATTN_LDS char*)lds[wave][buf][1]), lane);
+        // lanes 0-31: LSE of the chunk's queries, lanes 32-63: D (one 4-byte copy each)
+        const size_t qr = ((size_t)b * p.Hq + h) * p.N + min(i0 + l32, p.N - 1);
+        dma4(hh ? (const void*)(p.dsum + qr) : (const void*)(p.lse + qr),
+             lds_addr((ATTN_LDS float*)stat[wave][buf]));
+    };
+    auto compute = [&](int it, int buf, bool more) __attribute__((always_inline)) {
+        const int i0 = (qc0 + it % per_head) * kBC;
+        // this chunk's tiles and statistics are in LDS (the next chunk's 17 copies may stay in flight)
+        if (more) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // S = Q K^T and dP = dO V^T: lane = key, registers = queries 8 (r / 4) + 4 hh + r % 4
+        bf16x8 af[8];
+        f32x16 s = f32x16{}, dp = f32x16{};
+        lds_row_frags((const ATTN_LDS char*)lds[wave][buf][0], lane, af);
 #pragma unroll
-            for (int st = 0; st < 8; ++st) s = mfma_bf16(af[st], kf[st], s);
-            row_frags(p.dout + qh * kBD, i0, p.N, lane, af);
-            f32x16 dp = f32x16{};
+        for (int st = 0; st < 8; ++st) s = mfma_bf16(af[st], kf[st], s);
+        lds_row_frags((const ATTN_LDS char*)lds[wave][buf][1], lane, af);
 #pragma unroll
-            for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], vf[st], dp);
-            bf16x8 pk[2], sk[2];
+        for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], vf[st], dp);
+        bf16x8 pk[2], sk[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qrow = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const int qc = min(qrow, p.N - 1);
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int q4 = 8 * r4 + 4 * hh;   // queries q4 .. q4 + 3 of the chunk
+            const f32x4 l4 = *(const ATTN_LDS f32x4*)((const ATTN_LDS float*)stat[wave][buf] + q4);
+            const f32x4 d4 = *(const ATTN_LDS f32x4*)((const ATTN_LDS float*)stat[wave][buf] + kBC + q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * r4 + e, qrow = i0 + q4 + e;
                 const bool ok = qrow < p.N && key < p.N && (!p.causal || key <= qrow);
-                const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - p.lse[qh + qc] * kLog2e) : 0.f;
+                const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - l4[e] * kLog2e) : 0.f;
                 pk[r >> 3][r & 7] = (__bf16)pr;
-                sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - p.dsum[qh + qc]));
+                sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - d4[e]));
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the Q and dO tiles are in LDS
-            tr_gemm((const ATTN_LDS char*)lds[wave][1], ofs, pk, dv);   // dV^T += dO^T P
-            tr_gemm((const ATTN_LDS char*)lds[wave][0], ofs, sk, dk);   // dK^T += Q^T dS
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next refill
         }
+        tr_gemm((const ATTN_LDS char*)lds[wave][buf][1], ofs, pk, dv);   // dV^T += dO^T P
+        tr_gemm((const ATTN_LDS char*)lds[wave][buf][0], ofs, sk, dk);   // dK^T += Q^T dS
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the buffers are refilled
+    };
+    if (total > 0) issue(0, 0);
+    int it = 0;
+    for (; it + 1 < total; it += 2) {
+        issue(it + 1, 1);
+        compute(it, 0, true);
+        const bool more = it + 2 < total;
+        if (more) issue(it + 2, 0);
+        compute(it + 1, 1, more);
     }
+    if (it < total) compute(it, 0, false);
     store_rows(p.dk + kvh, j0, p.N, lane, dk, p.scale);
     store_rows(p.dv + kvh, j0, p.N, lane, dv, 1.f);
 }
 
-// dQ: one wave per (batch, query head, 32-query block).
+// dQ: one wave per (batch, query head, 32-query block). The next key chunk's
+// K and V tiles are requested before the current chunk is computed (two LDS
+// buffer pairs, the loop unrolled by two); K and V fragments are read from them.
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[4][kBC * Tile<kBD>::ROW_BYTES];   // per wave: K
+    __shared__ __attribute__((aligned(1024))) char lds[4][2][2][kBC * Tile<kBD>::ROW_BYTES];   // wave, buffer, K / V
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nqb = (p.N + kBC - 1) / kBC;
@@ -187,7 +226,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     if (wid >= p.B * p.Hq * nqb) return;
     const int qb = wid % nqb, h = (wid / nqb) % p.Hq, b = wid / (nqb * p.Hq);
     const int g = h / p.G;
-    const int l32 = lane & 31;
+    const int l32 = lane & 31, hh = lane >> 5;
     const int i0 = qb * kBC;
     const size_t qh = ((size_t)b * p.Hq + h) * p.N;
     const size_t kvh = ((size_t)b * p.Hkv + g) * p.N * kBD;
@@ -197,25 +236,30 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const int qrow = i0 + l32;
     const float lse2 = p.lse[qh + min(qrow, p.N - 1)] * kLog2e;
     const float dd = p.dsum[qh + min(qrow, p.N - 1)];
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no compiler-counted load stays pending into the loop
     int ofs[4];
     tr_offsets(lane, ofs);
-    const unsigned kt = lds_addr((ATTN_LDS char*)lds[wave]);
     f32x16 dq[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dq[t] = f32x16{};
-    const int hh = lane >> 5;
     const int nkc = p.causal ? min(qb + 1, (p.N + kBC - 1) / kBC) : (p.N + kBC - 1) / kBC;
-    for (int kc = 0; kc < nkc; ++kc) {
+
+    auto issue = [&](int kc, int buf) __attribute__((always_inline)) {
+        tile_to_lds(p.k + kvh, kc * kBC, p.N, lds_addr((ATTN_LDS char*)lds[wave][buf][0]), lane);
+        tile_to_lds(p.v + kvh, kc * kBC, p.N, lds_addr((ATTN_LDS char*)lds[wave][buf][1]), lane);
+    };
+    auto compute = [&](int kc, int buf, bool more) __attribute__((always_inline)) {
         const int j0 = kc * kBC;
-        tile_to_lds(p.k + kvh, j0, p.N, kt, lane);
-        bf16x8 af[8];
+        // this chunk's K and V tiles are in LDS (the next chunk's 16 copies may stay in flight)
+        if (more) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         // S^T = K Q^T, dP^T = V dO^T: lane = query, registers = keys 8 (r / 4) + 4 hh + r % 4
-        row_frags(p.k + kvh, j0, p.N, lane, af);
-        f32x16 s = f32x16{};
+        bf16x8 af[8];
+        f32x16 s = f32x16{}, dp = f32x16{};
+        lds_row_frags((const ATTN_LDS char*)lds[wave][buf][0], lane, af);
 #pragma unroll
         for (int st = 0; st < 8; ++st) s = mfma_bf16(af[st], qf[st], s);
-        row_frags(p.v + kvh, j0, p.N, lane, af);
-        f32x16 dp = f32x16{};
+        lds_row_frags((const ATTN_LDS char*)lds[wave][buf][1], lane, af);
 #pragma unroll
         for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], df[st], dp);
         bf16x8 sk[2];
@@ -226,10 +270,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
             const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - lse2) : 0.f;
             sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dd));
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the K tile is in LDS
-        tr_gemm((const ATTN_LDS char*)lds[wave], ofs, sk, dq);   // dQ^T += K^T dS^T
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        tr_gemm((const ATTN_LDS char*)lds[wave][buf][0], ofs, sk, dq);   // dQ^T += K^T dS^T
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the buffer is refilled
+    };
+    if (nkc > 0) issue(0, 0);
+    int kc = 0;
+    for (; kc + 1 < nkc; kc += 2) {
+        issue(kc + 1, 1);
+        compute(kc, 0, true);
+        const bool more = kc + 2 < nkc;
+        if (more) issue(kc + 2, 0);
+        compute(kc + 1, 1, more);
     }
+    if (kc < nkc) compute(kc, 0, false);
     store_rows(p.dq + qh * kBD, i0, p.N, lane, dq, p.scale);
 }
 
