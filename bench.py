@@ -39,12 +39,14 @@ CSRC = os.path.join(ROOT, "tiled_attention_05_amd", "csrc")
 # kernel sources whose hash keys the measured HBM traffic of a profile summary
 KERNEL_SOURCES = {"bf16": ["attn_fwd_bf16.hip", "fwd_common.h", "common.h", "fwd_params.h"],
                   "decode": ["decode.hip", "fwd_common.h", "common.h"],
+                  "bwd": ["bwd.hip", "fwd_common.h", "common.h"],
                   "fp8": ["fp8.hip", "fwd_common.h", "common.h", "fwd_params.h"],
                   "f32": ["attn_fwd_f32.hip", "fwd_common.h", "common.h", "fwd_params.h"]}
 PROFILE_SUMMARY = {2: "profiles/fwd_bf16_causal_prefill_b4_h32_n4096_d128.md",
                    5: "profiles/fwd_fp8_dense_b4_h16_n8192_d128.md",
                    6: "profiles/fwd_bf16_varlen_causal_t32768_h32x8_d128.md",
-                   7: "profiles/decode_paged_b64_h32x8_d128_len1k-8k.md"}
+                   7: "profiles/decode_paged_b64_h32x8_d128_len1k-8k.md",
+                   8: "profiles/bwd_bf16_causal_b4_h32_n4096_d128.md"}
 
 
 def sources_hash(kind):
@@ -197,6 +199,7 @@ def bench_backward(w, args):
     ms_kernel = evs[0].elapsed_time(evs[-1]) / args.steps
     per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     achieved = fl / (ms_kernel * 1e-3) / 1e12
+    traffic, _ = measured_profile(args.workload, "bwd")
     out = {
         "metric": "attention bwd TFLOPS (2.5x the mask-adjusted forward FLOPs)",
         "value": round(fl / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -205,7 +208,7 @@ def bench_backward(w, args):
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "mask": mask_name(w.mask), "flops_per_step": fl, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": None,
+                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
                      "kernel_ms": round(ms_kernel, 4), "kernel_ms_median": round(per_launch[len(per_launch) // 2], 4),
                      "kernel_ms_min": round(per_launch[0], 4)},
     }

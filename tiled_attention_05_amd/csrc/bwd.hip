@@ -34,21 +34,22 @@ struct BwdParams {
 
 constexpr int kBD = 128, kBC = 32;   // head dim, rows per block / chunk
 
-// D_i = sum_c dO_ic O_ic (float32), one wave per 64 rows: lane = row.
+// D_i = sum_c dO_ic O_ic (float32): 16 lanes per row (16 bytes each, so a
+// wave reads 4 whole rows per instruction), 16 rows per 256-thread block.
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdParams p) {
-    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t rows = (size_t)p.B * p.Hq * p.N;
-    if (row >= rows) return;
-    const bf16x8* a = (const bf16x8*)(p.dout + row * kBD);
-    const bf16x8* b = (const bf16x8*)(p.o + row * kBD);
+    const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int c = threadIdx.x & 15;
     float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < kBD / 8; ++c) {
-        const bf16x8 x = a[c], y = b[c];
+    if (row < rows) {
+        const bf16x8 x = *(const bf16x8*)(p.dout + row * kBD + 8 * c);
+        const bf16x8 y = *(const bf16x8*)(p.o + row * kBD + 8 * c);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
     }
-    p.dsum[row] = s;
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);   // within the 16-lane group
+    if (row < rows && c == 0) p.dsum[row] = s;
 }
 
 // Transposed-read offsets of the prefill kernel (one 32-row tile): lane L of a
@@ -297,7 +298,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.N = N;
     p.scale = scale; p.scale_log2 = scale * kLog2e; p.causal = causal;
     const size_t rows = (size_t)p.B * p.Hq * p.N;
-    hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nb = (p.N + kBC - 1) / kBC;
