@@ -396,7 +396,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         const float alpha = need ? fast_exp2(m - mn) : 1.f;
         m = need ? mn : m;
         const float mneg = -m;
-        float ls0 = 0.f, ls1 = 0.f, ls2 = 0.f, ls3 = 0.f;
+        float ls0 = -0.f, ls1 = -0.f, ls2 = -0.f, ls3 = -0.f;   // -0 + p folds to p
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -414,6 +414,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
             pin(pf[kb][1]);
         }
         l = l * alpha + ((ls0 + ls1) + (ls2 + ls3));
+        // take the sums here, while the other wave of the SIMD is in its matrix
+        // phase (left alone, the compiler sinks them below GEMM0, onto the
+        // path to the next barrier)
+        pin(l);
         rescale_by = alpha;
         rescale_any = __builtin_amdgcn_ballot_w64(need) != 0;
         if (__builtin_expect(rescale_any, 0)) {   // rare: the reference max moved

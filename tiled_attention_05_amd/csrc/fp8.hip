@@ -443,6 +443,9 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
             }
         pin(pf);   // P is complete here; GEMM1 reads it after wait states
         l = l * alpha + ((ls0 + ls1) + (ls2 + ls3)) * fast_exp2(-bias);
+        // take the sums here, while the other wave of the SIMD is in its matrix
+        // phase (left alone, the compiler sinks them into this wave's own)
+        pin(l);
         rescale_by = alpha;
         rescale_any = __builtin_amdgcn_ballot_w64(need) != 0;
         if (__builtin_expect(rescale_any, 0)) {   // rare: the reference max moved
