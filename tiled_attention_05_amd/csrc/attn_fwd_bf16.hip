@@ -98,8 +98,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // register is refilled two products after the product that read it.
     constexpr int LA = ATTN_LDS_AHEAD, NB = LA + 2;
     static_assert(LA >= 1 && LA <= 7, "read-ahead 1..7 (lgkmcnt range)");
-    using Copy = TileCopy<D, NW>;
-    constexpr int LOADS_PER_TILE = 2 * Copy::ROUNDS + (DOC ? 1 : 0);   // per wave
+    // Without modifiers or document ids, group A issues all the copies (its
+    // waves wait at the barrier while group B finishes its matrix phase, so
+    // the issue time is hidden there) and group B none; else every wave
+    // issues its share.
+    constexpr bool A_ONLY = !MODS && !DOC;
+    using Copy = TileCopy<D, A_ONLY ? NW / 2 : NW>;
+    constexpr int LOADS_PER_TILE = 2 * Copy::ROUNDS + (DOC ? 1 : 0);   // per copying wave
 
     __shared__ __attribute__((aligned(1024))) char tiles_lds[(NKB + NVB) * T::BYTES];
     __shared__ __attribute__((aligned(16))) int docs_lds[DOC ? NVB * NW * BN : 4];
@@ -456,6 +461,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // waves read K(i), V(i - 1), the document ids of tiles i - 1 and i, and
     // refill K(i - 1), V(i - 2): never a buffer being read.
     auto copies = [&](int i) __attribute__((always_inline)) {
+        if (A_ONLY && group_b) return;
         if (i + PF < n_tiles) {
             tile_k(i + PF);
             tile_v(i + PF);
@@ -463,7 +469,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     };
     auto barrier_and_copy = [&](int i, bool copy = true) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        static_assert(2 * LOADS_PER_TILE <= 15, "vmcnt immediate");
+        static_assert((PF - 1) * LOADS_PER_TILE <= 15, "vmcnt immediate");
         const int ahead = min(PF - 1, n_tiles - 1 - i);   // later tiles whose copies may stay in flight
         if (PF >= 3 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * LOADS_PER_TILE));
         else if (PF >= 2 && ahead >= 1) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
@@ -506,7 +512,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     if (n_tiles > 0) {
 #pragma unroll
         for (int i = 0; i < PF; ++i)
-            if (i < n_tiles) {
+            if (i < n_tiles && !(A_ONLY && group_b)) {
                 tile_k(i);
                 tile_v(i);
             }
