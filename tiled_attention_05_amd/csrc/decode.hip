@@ -70,10 +70,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = qv ? *(const bf16x8*)(qr + 16 * s) : bf16x8{};
     }
-    // row of key `key` (clamped into the sequence) in a cache
-    auto row_of = [&](const __bf16* cache, int key) __attribute__((always_inline)) {
+    // The 32 keys of chunk c lie in pages 2 c and 2 c + 1 (keys past the end
+    // are clamped to the last one, whose page is one of the two). Both table
+    // entries are read once per chunk through the scalar cache (wave-uniform
+    // index): a vector load of the table would have to be waited for with a
+    // vmcnt that also drains every copy already in flight.
+    const int last_page = (L - 1) / kPage;
+    auto pages = [&](int c, int& pg0, int& pg1) __attribute__((always_inline)) {
+        const ATTN_CONST int32_t* t = (const ATTN_CONST int32_t*)table;
+        pg0 = t[2 * c];
+        pg1 = t[min(2 * c + 1, last_page)];
+    };
+    // row of key `key` of chunk c (clamped into the sequence) in a cache
+    auto row_of = [&](const __bf16* cache, int c, int pg0, int pg1, int key) __attribute__((always_inline)) {
         const int kk = min(key, L - 1);
-        return cache + (size_t)table[kk / kPage] * block_elems + head_off + (size_t)(kk % kPage) * kDD;
+        const int pg = (kk / kPage == 2 * c) ? pg0 : pg1;
+        return cache + (size_t)pg * block_elems + head_off + (size_t)(kk % kPage) * kDD;
     };
     // V transposed reads (as the prefill kernel, one 32-key block): lane L of a
     // 16-lane group addresses row 4 hh + L / 4 (+ 16 u, + 8 for the high half),
@@ -89,18 +101,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
 
     bf16x8 kf[8];
-    auto load_k = [&](int c) __attribute__((always_inline)) {
-        const __bf16* kr = row_of(p.kc, c * kCh + l32) + 8 * hh;
+    auto load_k = [&](int c, int pg0, int pg1) __attribute__((always_inline)) {
+        const __bf16* kr = row_of(p.kc, c, pg0, pg1, c * kCh + l32) + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 8; ++s) kf[s] = *(const bf16x8*)(kr + 16 * s);
     };
     // V tile of chunk c into buffer c & 1: slot i 64 + lane = (row, 16-byte chunk), swizzled like the prefill tile
-    auto load_v = [&](int c) __attribute__((always_inline)) {
+    auto load_v = [&](int c, int pg0, int pg1) __attribute__((always_inline)) {
         const unsigned base = lds_addr((ATTN_LDS char*)vt_lds[wave][c & 1]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int slot = i * 64 + lane, r = slot >> 4, pc = slot & 15;
-            const __bf16* src = row_of(p.vc, c * kCh + r) + 8 * (pc ^ T::swz_v(r));
+            const __bf16* src = row_of(p.vc, c, pg0, pg1, c * kCh + r) + 8 * (pc ^ T::swz_v(r));
             dma16(src, base + i * 1024);
         }
     };
@@ -111,8 +123,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     float m = kDecNoMax, l = 0.f;
 
     if (c0 < c1) {
-        load_k(c0);
-        load_v(c0);
+        int pg0, pg1;
+        pages(c0, pg0, pg1);
+        load_k(c0, pg0, pg1);
+        load_v(c0, pg0, pg1);
     }
     for (int c = c0; c < c1; ++c) {
         // this chunk's K registers and V tile have landed; then the next chunk's loads go out
@@ -121,8 +135,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int st = 0; st < 8; ++st) s = mfma_bf16(kf[st], qf[st], s);
         if (c + 1 < c1) {
-            load_k(c + 1);
-            load_v(c + 1);
+            int pg0, pg1;
+            pages(c + 1, pg0, pg1);
+            load_k(c + 1, pg0, pg1);
+            load_v(c + 1, pg0, pg1);
         }
         const int kv0 = c * kCh;
         float mx = -INFINITY;
