@@ -85,24 +85,27 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(const __bf16* __restri
 
     float x[STEPS][4][8];   // [step][j][e]: dim 8c + 32j + e
     float am = 0.f;
+    // The rows of every step are loaded first, all loads in flight together;
+    // rows past N read row N - 1 and are zeroed (no branch around the loads).
+    bf16x8 raw[STEPS][4];
+#pragma unroll
+    for (int it = 0; it < STEPS; ++it) {
+        const int row = tile * kFp8Tile + it * 64 + wave * 16 + tq;
+        const __bf16* rp = src + ((size_t)bh * N + min(row, N - 1)) * D + 8 * c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[it][j] = *(const bf16x8*)(rp + 32 * j);
+    }
 #pragma unroll
     for (int it = 0; it < STEPS; ++it) {
         const int t = it * 64 + wave * 16 + tq;   // token within the tile
         const int row = tile * kFp8Tile + t;
         float (*y)[8] = x[it];
-        if (row < N) {
-            const __bf16* rp = src + ((size_t)bh * N + row) * D + 8 * c;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 w = *(const bf16x8*)(rp + 32 * j);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[j][e] = (float)w[e];
-            }
-        } else {
+        {
+            const bool in = row < N;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) y[j][e] = 0.f;
+                for (int e = 0; e < 8; ++e) y[j][e] = in ? (float)raw[it][j][e] : 0.f;
         }
         if (rope && row < N) {
             // pair (i, i + 64) = (j, j + 2) of this lane, i = 8c + 32j + e, j < 2
