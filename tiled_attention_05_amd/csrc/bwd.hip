@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nkb = (p.N + kBC - 1) / kBC, nkg = (nkb + 3) / 4;
-    const int kg = blockIdx.x % nkg, g = (blockIdx.x / nkg) % p.Hkv, b = blockIdx.x / (nkg * p.Hkv);
+    // heavy groups first: under a causal mask the first key blocks see the most query chunks
+    const int kg = blockIdx.x / (p.B * p.Hkv), g = blockIdx.x % p.Hkv, b = (blockIdx.x / p.Hkv) % p.B;
     const int kb = 4 * kg + wave;   // may be >= nkb: then every key of the block is masked
     const int l32 = lane & 31, hh = lane >> 5;
     const int j0 = kb * kBC;
@@ -242,7 +243,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nqb = (p.N + kBC - 1) / kBC, nqg = (nqb + 3) / 4;
-    const int qg = blockIdx.x % nqg, h = (blockIdx.x / nqg) % p.Hq, b = blockIdx.x / (nqg * p.Hq);
+    // heavy groups first: under a causal mask the last query blocks see the most key chunks
+    const int qg = nqg - 1 - (int)(blockIdx.x / (p.B * p.Hq)), h = blockIdx.x % p.Hq, b = (blockIdx.x / p.Hq) % p.B;
     const int qb = 4 * qg + wave;   // may be >= nqb: then every query of the block is masked
     const int g = h / p.G;
     const int l32 = lane & 31, hh = lane >> 5;
