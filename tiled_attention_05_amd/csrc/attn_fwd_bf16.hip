@@ -364,19 +364,37 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
                     }
             }
         }
+        // ALiBi: the bias slope (j - row) = slope jc + slope (j0 + 4 hh - row)
+        // with jc = 32 kb + 8 (r / 4) + r % 4 (key within tile less the lane's
+        // 4 hh): the first part is added here, one FMA with a literal per
+        // score; the second, the same for all scores of the lane, is folded
+        // into the row max and the exponent reference (alibi_lane).
+        if (full) {   // no element mask
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
-                if ((r & 3) == 0) pin(sacc[kb]);   // four elements at a time
-                const float x = sacc[kb][r];
-                float y = SOFTCAP ? x : x * c;
-                if (ALIBI) y -= slope_l2 * (float)(row - (j0 + jl));
-                bool ok = jl <= jl_hi && jl >= jl_lo;
-                if (DOC && !full) ok &= dk[kb][r] == doc_i;
-                sacc[kb][r] = ok ? y : -INFINITY;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    if ((r & 3) == 0) pin(sacc[kb]);   // four elements at a time
+                    const float x = sacc[kb][r];
+                    float y = SOFTCAP ? x : x * c;
+                    if (ALIBI) y = __builtin_fmaf((float)(32 * kb + 8 * (r >> 2) + (r & 3)), slope_l2, y);
+                    sacc[kb][r] = y;
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
+                    if ((r & 3) == 0) pin(sacc[kb]);
+                    const float x = sacc[kb][r];
+                    float y = SOFTCAP ? x : x * c;
+                    if (ALIBI) y = __builtin_fmaf((float)(32 * kb + 8 * (r >> 2) + (r & 3)), slope_l2, y);
+                    bool ok = jl <= jl_hi && jl >= jl_lo;
+                    if (DOC) ok &= dk[kb][r] == doc_i;
+                    sacc[kb][r] = ok ? y : -INFINITY;
+                }
+        }
     };
 
     float rescale_by = 1.f;      // output factor of the last softmax (1 for most rows)
@@ -395,12 +413,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
             a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
         }
         a0 = max3(a0, sacc[0][15], max2(a1, sacc[1][15]));
-        const float mx = xhalf_max(a0) * ce;
+        // lane part of the ALiBi bias (see prepare_scores), 0 without ALiBi
+        const float alibi_lane = ALIBI ? slope_l2 * (float)(kt * BN + 4 * hh - row) : 0.f;
+        const float mx = xhalf_max(a0 + alibi_lane) * ce;
         const float mn = max2(m, mx);
         const bool need = mn > m + kLazyTau;
         const float alpha = need ? fast_exp2(m - mn) : 1.f;
         m = need ? mn : m;
-        const float mneg = -m;
+        const float mneg = alibi_lane - m;
         float ls0 = -0.f, ls1 = -0.f, ls2 = -0.f, ls3 = -0.f;   // -0 + p folds to p
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
