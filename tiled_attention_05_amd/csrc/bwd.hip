@@ -17,6 +17,7 @@
 // per-wave LDS tile in the prefill kernel's swizzled layout and its transposed
 // reads, and the probabilities are packed in the matching permuted order.
 #include <climits>
+#include <type_traits>
 
 #include "fwd_common.h"
 
@@ -271,6 +272,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     };
     auto compute = [&](int kc, int buf) __attribute__((always_inline)) {
         const int j0 = kc * kBC;
+        // every (query, key) pair of the chunk allowed (see the dK / dV kernel)
+        const bool full = i0 + kBC <= p.N && j0 + kBC <= p.N && (!p.causal || j0 + kBC - 1 <= i0);
         // S^T = K Q^T, dP^T = V dO^T: lane = query, registers = keys 8 (r / 4) + 4 hh + r % 4
         bf16x8 af[8];
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -281,13 +284,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], df[st], dp);
         bf16x8 sk[2];
+        auto probs = [&](auto mask_c) __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = qrow < p.N && key < p.N && (!p.causal || key <= qrow);
-            const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - lse2) : 0.f;
-            sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dd));
-        }
+            for (int r = 0; r < 16; ++r) {
+                const int key = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool ok = !MASK || (qrow < p.N && key < p.N && (!p.causal || key <= qrow));
+                const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - lse2) : 0.f;
+                sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dd));
+            }
+        };
+        if (full) probs(std::integral_constant<bool, false>{});
+        else probs(std::integral_constant<bool, true>{});
         tr_gemm((const ATTN_LDS char*)lds[buf][0], ofs, sk, dq);   // dQ^T += K^T dS^T
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next barrier
     };
