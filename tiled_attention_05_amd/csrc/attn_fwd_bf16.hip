@@ -118,7 +118,16 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // ---- work item: heavy (late) query tiles first for causal balance
     const int wid = blockIdx.x;
     const int qt = p.n_qt - 1 - wid / p.n_bh;
-    const int bh = wid % p.n_bh;
+    // (batch, head) slot j of the grid row. With grouped heads, the heads
+    // of one key / value head are put 8 slots apart, i.e. on the same XCD
+    // under round-robin dispatch, so they share its L2 for the K / V tiles.
+    const int j = wid % p.n_bh;
+    int bh = j;
+    const int n_u = p.B * p.Hkv;   // key / value heads
+    if (p.group > 1 && n_u % 8 == 0) {
+        const int u = (j / (8 * p.group)) * 8 + j % 8, q = (j / 8) % p.group;
+        bh = (u / p.Hkv) * p.Hq + (u % p.Hkv) * p.group + q;
+    }
     const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.group;
     const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
     const bool causal = p.mask & kMaskCausal, windowed = p.mask & kMaskWindow;
