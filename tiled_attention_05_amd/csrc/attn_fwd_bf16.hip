@@ -117,11 +117,20 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 
     // ---- work item: heavy (late) query tiles first for causal balance
     const int wid = blockIdx.x;
-    const int qt = p.n_qt - 1 - wid / p.n_bh;
-    // (batch, head) slot j of the grid row. With grouped heads, the heads
-    // of one key / value head are put 8 slots apart, i.e. on the same XCD
-    // under round-robin dispatch, so they share its L2 for the K / V tiles.
-    const int j = wid % p.n_bh;
+    int qt = p.n_qt - 1 - wid / p.n_bh;
+    // (batch, head) slot j. Round-robin dispatch puts workgroup w on XCD
+    // w % 8. With xgrp > 0 each XCD takes its heads xgrp at a time, all
+    // query tiles of those heads (heaviest first) before the next ones, so
+    // the tiles in flight on one XCD read the same few K / V heads from its
+    // L2. With grouped heads, the heads of one key / value head are put 8
+    // slots apart, i.e. on the same XCD, for the same reason.
+    int j = wid % p.n_bh;
+    if (p.xgrp > 0) {
+        const int x = wid % 8, k = wid / 8, per = p.xgrp * p.n_qt;
+        const int r = k % per;
+        qt = p.n_qt - 1 - r / p.xgrp;
+        j = x + 8 * ((k / per) * p.xgrp + r % p.xgrp);
+    }
     int bh = j;
     const int n_u = p.B * p.Hkv;   // key / value heads
     if (p.group > 1 && n_u % 8 == 0) {
@@ -591,6 +600,17 @@ static hipError_t launch_bf16_inst(const FwdParams& p0, hipStream_t st) {
     constexpr int BM = 256;
     p.n_qt = (p.Nq + BM - 1) / BM;
     p.n_bh = p.B * p.Hq;
+    // Head groups per XCD: as many heads as fill its resident workgroups
+    // (32 CUs, one workgroup each), when the heads split evenly over the 8
+    // XCDs and into groups of at least two. With one head per group (long
+    // sequences) the plain order measured faster.
+    p.xgrp = 0;
+    if (p.n_bh % 8 == 0) {
+        const int per_xcd = p.n_bh / 8;
+        int g = 32 / p.n_qt;
+        while (g > 1 && per_xcd % g) --g;
+        p.xgrp = g >= 2 ? g : 0;
+    }
     hipLaunchKernelGGL((fwd_bf16_kernel<D, SC, AL, DC>), dim3(p.n_qt * p.n_bh), dim3(512), 0, st, p);
     return hipGetLastError();
 }

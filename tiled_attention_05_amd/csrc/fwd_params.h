@@ -24,6 +24,7 @@ struct FwdParams {
     int n_qt;               // query tiles per (b, h)
     int n_bh;               // B * Hq
     int npad;               // fp8: token count padded to the scale tile
+    int xgrp;               // bf16: heads per XCD in one dispatch group, 0 = plain order
 };
 
 }  // namespace attn
