@@ -29,8 +29,9 @@ def _close(g, ref, label):
     assert mx <= 2e-2 and mn <= 1e-2, label
 
 
+# the last two have 16 and 32 heads: their grids are dispatched in head groups per XCD
 CASES = [(1, 2, 2, 64, 0), (1, 2, 2, 200, 1), (2, 4, 2, 300, 1), (1, 8, 1, 257, 0), (1, 2, 2, 1, 1),
-         (1, 4, 4, 1000, 1)]
+         (1, 4, 4, 1000, 1), (2, 8, 8, 300, 1), (1, 32, 16, 200, 0)]
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,mask", CASES, ids=[f"{c[1]}x{c[2]}-N{c[3]}-m{c[4]}" for c in CASES])

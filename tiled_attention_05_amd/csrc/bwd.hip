@@ -31,7 +31,24 @@ struct BwdParams {
     int B, Hq, Hkv, G, N;
     float scale, scale_log2;
     int causal;
+    int xg_kv, xg_q;   // heads per XCD dispatch group of the dK/dV and dQ grids, 0 = plain order
 };
+
+// Work item of a grid of n_heads x ng workgroups, group index heaviest first
+// (the caller maps it to its blocks). Round-robin dispatch puts workgroup w
+// on XCD w % 8; with xg > 0 each XCD takes its heads xg at a time, all groups
+// of those heads before the next ones, so the workgroups in flight on one XCD
+// share the few heads' rows in its L2.
+__device__ inline void grid_item(int w, int n_heads, int ng, int xg, int& head, int& grp) {
+    if (xg > 0) {
+        const int x = w % 8, k = w / 8, per = xg * ng, r = k % per;
+        grp = r / xg;
+        head = x + 8 * ((k / per) * xg + r % xg);
+    } else {
+        grp = w / n_heads;
+        head = w % n_heads;
+    }
+}
 
 constexpr int kBD = 128, kBC = 32;   // head dim, rows per block / chunk
 
@@ -161,7 +178,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nkb = (p.N + kBC - 1) / kBC, nkg = (nkb + 3) / 4;
     // heavy groups first: under a causal mask the first key blocks see the most query chunks
-    const int kg = blockIdx.x / (p.B * p.Hkv), g = blockIdx.x % p.Hkv, b = (blockIdx.x / p.Hkv) % p.B;
+    int kg, bg;
+    grid_item(blockIdx.x, p.B * p.Hkv, nkg, p.xg_kv, bg, kg);
+    const int g = bg % p.Hkv, b = bg / p.Hkv;
     const int kb = 4 * kg + wave;   // may be >= nkb: then every key of the block is masked
     const int l32 = lane & 31, hh = lane >> 5;
     const int j0 = kb * kBC;
@@ -245,7 +264,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nqb = (p.N + kBC - 1) / kBC, nqg = (nqb + 3) / 4;
     // heavy groups first: under a causal mask the last query blocks see the most key chunks
-    const int qg = nqg - 1 - (int)(blockIdx.x / (p.B * p.Hq)), h = blockIdx.x % p.Hq, b = (blockIdx.x / p.Hq) % p.B;
+    int qg, bh;
+    grid_item(blockIdx.x, p.B * p.Hq, nqg, p.xg_q, bh, qg);
+    qg = nqg - 1 - qg;
+    const int h = bh % p.Hq, b = bh / p.Hq;
     const int qb = 4 * qg + wave;   // may be >= nqb: then every query of the block is masked
     const int g = h / p.G;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -324,6 +346,17 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     if (e != hipSuccess) return e;
     // one workgroup per 4 consecutive blocks of 32 rows of one head
     const long long ng = ((p.N + kBC - 1) / kBC + 3) / 4;
+    // Dispatch groups of as many heads as fill an XCD's resident workgroups
+    // (32 CUs, two workgroups each), when the heads split evenly over the 8
+    // XCDs and into groups of at least two.
+    auto xcd_group = [&](long long n_heads) {
+        if (n_heads % 8 || ng > 32) return 0;
+        int g = (int)(64 / ng);
+        while (g > 1 && (n_heads / 8) % g) --g;
+        return g >= 2 ? g : 0;
+    };
+    p.xg_kv = xcd_group((long long)p.B * p.Hkv);
+    p.xg_q = xcd_group((long long)p.B * p.Hq);
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((long long)p.B * p.Hkv * ng)), dim3(256), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
