@@ -95,11 +95,39 @@ def test_prepare_matches_oracle(N, Hq, Hkv):
               flush=True)
 
 
-@pytest.mark.parametrize("N,Hq,Hkv", [(300, 2, 2), (640, 4, 2), (64, 1, 1), (1, 1, 1)])
+def _pack_oracle(w, x):
+    """Packed e4m3 buffers (the layout attn_fp8_prepare writes) holding the
+    oracle's own codes and scales, so that the forward is checked on exactly
+    the codes the emulation uses: the prepare kernel rotates in float32, and a
+    code it rounds the other way at a midpoint moves that row's LSE by up to
+    about 1e-3 (one e4m3 step of an outlier channel); the prepare tests cover
+    those codes separately."""
+    signs = x["signs"].numpy()
+    q64, k64, v64 = (x[n].double().numpy() for n in ("q", "k", "v"))
+    parts = [(F8.quantize_rows(F8.rotate(q64, signs)), w.Hq, False),
+             (F8.quantize_rows(F8.rotate(k64, signs)), w.Hkv, False),
+             (F8.quantize_rows(v64), w.Hkv, True)]
+    bufs = []
+    for (codes, scales), H, tr in parts:
+        buf = torch.zeros(_lib.attn_fp8_buffer_bytes(w.B, H, w.N, w.d), dtype=torch.uint8)
+        cv, sv = _lib.fp8_unpack(buf, w.B, H, w.N, w.d, transposed=tr)
+        c = torch.from_numpy(codes)
+        if tr:
+            cv[:, :, :, :w.N] = c.transpose(2, 3)
+        else:
+            cv[:, :, :w.N] = c
+        sv.copy_(torch.from_numpy(scales))
+        bufs.append(buf.cuda())
+    return bufs
+
+
+# (1000, 16, 8): 16 heads, so the grid is dispatched in head groups per XCD
+@pytest.mark.parametrize("N,Hq,Hkv", [(300, 2, 2), (640, 4, 2), (64, 1, 1), (1, 1, 1), (1000, 16, 8)])
 def test_fp8_forward_small(N, Hq, Hkv):
     w = I.WORKLOADS[5].shrink(B=1, Hq=Hq, Hkv=Hkv, N=N)
     print(f"[case] fp8 fwd N={N} Hq={Hq} Hkv={Hkv}", flush=True)
-    x, (q8, k8, v8) = _prep(w)
+    x = I.inputs(w, None, "channels")
+    q8, k8, v8 = _pack_oracle(w, x)
     o, lse = _lib.fwd_fp8(q8, k8, v8, w.B, Hq, Hkv, N, 128, scale=w.scale)
     torch.cuda.synchronize()
     q64, k64, v64 = (x[n].double().numpy() for n in ("q", "k", "v"))

@@ -272,8 +272,16 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     const bool group_b = wave >= NW / 2;
     const int l32 = lane & 31, hh = lane >> 5;
     const int wid = blockIdx.x;
-    const int qt = p.n_qt - 1 - wid / p.n_bh;
-    const int bh = wid % p.n_bh;
+    int qt = p.n_qt - 1 - wid / p.n_bh;
+    int bh = wid % p.n_bh;
+    // With xgrp > 0 each XCD (workgroup w runs on XCD w % 8) takes its heads
+    // xgrp at a time, all query tiles of those heads before the next ones, so
+    // the tiles in flight on one XCD read the same K / V codes from its L2.
+    if (p.xgrp > 0) {
+        const int x = wid % 8, k = wid / 8, per = p.xgrp * p.n_qt, r = k % per;
+        qt = p.n_qt - 1 - r / p.xgrp;
+        bh = x + 8 * ((k / per) * p.xgrp + r % p.xgrp);
+    }
     const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.group;
     const int N = p.Nk, Np = p.npad, ntile = Np / kFp8Tile;
     const int q0 = qt * BM;
@@ -570,6 +578,14 @@ hipError_t launch_fwd_fp8(const FwdParams& p0, int d, hipStream_t st) {
     FwdParams p = p0;
     p.n_qt = (p.Nq + 255) / 256;
     p.n_bh = p.B * p.Hq;
+    // Head groups per XCD: as many heads as fill its 32 resident workgroups
+    // (at least one), when the heads split evenly over the 8 XCDs and groups.
+    p.xgrp = 0;
+    if (p.n_bh % 8 == 0) {
+        int g = max(1, 32 / p.n_qt);
+        while (g > 1 && (p.n_bh / 8) % g) --g;
+        p.xgrp = g;
+    }
     if (p.Nk % BN) hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3(p.n_qt * p.n_bh), dim3(512), 0, st, p);
     else hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3(p.n_qt * p.n_bh), dim3(512), 0, st, p);
     return hipGetLastError();
