@@ -219,7 +219,9 @@ int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window,
  *              blocks (device data: a precondition, not checked).
  * num_splits : 1..256; with more than one, workspace is device float32 of
  *              attn_decode_workspace_floats(B, Hq, d, num_splits) entries
- *              (caller-owned scratch, overwritten); NULL is allowed with 1.
+ *              (caller-owned scratch, overwritten: the splits' partial outputs
+ *              and LSEs, and the order in which the sequences are launched,
+ *              longest first); NULL is allowed with 1.
  * Supported  : dtype ATTN_BF16, d = 128, block_size = 16, Hq / Hkv <= 32.
  * Errors     : ATTN_ERR_INVALID_ARG for NULL q/k_cache/v_cache/block_table/
  *              seq_lens/o, sizes < 1, Hq % Hkv != 0, non-finite scale,

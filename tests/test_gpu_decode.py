@@ -20,6 +20,8 @@ CASES = [
     (2, 16, 8, [0, 77], 3),
     (1, 6, 3, [4097], 16),
     (3, 4, 2, [31, 32, 65], 8),
+    # equal and empty lengths: the sequences are launched longest first, ties by index
+    (9, 4, 2, [50, 300, 50, 0, 300, 7, 1000, 50, 0], 4),
 ]
 
 

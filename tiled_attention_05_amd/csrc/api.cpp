@@ -210,7 +210,8 @@ int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window, cons
 size_t attn_decode_workspace_floats(int B, int Hq, int d, int num_splits) {
     if (B < 1 || Hq < 1 || d < 1 || num_splits < 1) return 0;
     if (num_splits == 1) return 0;
-    return (size_t)B * Hq * num_splits * (d + 1);
+    // split outputs and LSEs, then one 32-bit word per sequence (launch order)
+    return (size_t)B * Hq * num_splits * (d + 1) + (size_t)B;
 }
 
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,

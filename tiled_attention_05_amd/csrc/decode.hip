@@ -33,12 +33,34 @@ struct DecodeParams {
     __bf16* o;               // [B][Hq][128]
     float* lse;              // [B][Hq] or null
     float* part;             // splits > 1: [B][Hq][splits][128] outputs, then [B][Hq][splits] LSEs
+    const int32_t* order;    // [B] sequences longest first, or null for the plain order
     int B, Hq, Hkv, G, max_blocks, splits;
     float scale_log2;
 };
 
 constexpr int kPage = 16, kDD = 128, kCh = 32;   // page size, head dim, keys per chunk
 constexpr float kDecNoMax = -1e30f;              // initial reference: finite, below any score
+constexpr int kOrderMax = 4096;                  // sequences the launch-order kernel ranks
+
+// Launch order of the sequences, longest cached length first (ties: lower
+// index first), so that the waves of the longest sequences start first and
+// the grid does not end on a few long waves. One workgroup: the lengths are
+// staged in LDS and every sequence counts the sequences ahead of it; the order
+// is strict and total, so the ranks are a permutation of 0 .. B - 1.
+__global__ __launch_bounds__(1024) void decode_order_kernel(const int32_t* lens, int32_t* order, int B) {
+    __shared__ int len_lds[kOrderMax];
+    for (int j = threadIdx.x; j < B; j += blockDim.x) len_lds[j] = lens[j];
+    __syncthreads();
+    for (int j = threadIdx.x; j < B; j += blockDim.x) {
+        const int lj = len_lds[j];
+        int rank = 0;
+        for (int c = 0; c < B; ++c) {
+            const int lc = len_lds[c];
+            rank += (lc > lj || (lc == lj && c < j)) ? 1 : 0;
+        }
+        order[rank] = j;
+    }
+}
 
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     using T = Tile<kDD>;
@@ -51,7 +73,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     if (wid >= p.B * p.Hkv * p.splits) return;   // whole waves; the kernel has no barrier
     const int split = wid % p.splits;
     const int kvh = (wid / p.splits) % p.Hkv;
-    const int b = wid / (p.splits * p.Hkv);
+    const int slot = wid / (p.splits * p.Hkv);
+    // (clamped: a sequence index outside 0 .. B - 1 can never be addressed)
+    const int b = p.order ? min(max(p.order[slot], 0), p.B - 1) : slot;
     const int l32 = lane & 31, hh = lane >> 5;
     const int L = p.lens[b];
     const int nch = (L + kCh - 1) / kCh;
@@ -241,9 +265,18 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
     p.o = (__bf16*)o;
     p.lse = lse;
     p.part = workspace;
+    p.order = nullptr;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.max_blocks = max_blocks; p.splits = splits;
     p.scale_log2 = scale * kLog2e;
     const long long waves = (long long)B * Hkv * splits;
+    if (splits > 1 && B <= kOrderMax) {
+        // the order lives after the split outputs and LSEs in the workspace
+        int32_t* order = (int32_t*)(workspace + (size_t)B * Hq * splits * (kDD + 1));
+        hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, st, lens, order, B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.order = order;
+    }
     hipLaunchKernelGGL(decode_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;

@@ -78,7 +78,7 @@ WORKLOADS = {
                 mask=MASK_CAUSAL, extra={"backward": True}),
     # one-token decode over a paged cache: 64 sequences of [1024, 8192] cached tokens, 16-token blocks
     7: Workload(7, "decode_paged_bf16", B=64, Hq=32, Hkv=8, N=8192, d=128, dtype="bf16",
-                extra={"decode": True, "len_range": (1024, 8192), "block": 16, "splits": 12}),
+                extra={"decode": True, "len_range": (1024, 8192), "block": 16, "splits": 8}),
     # packed variable-length batch: sequences of [128, 4096] tokens, causal within each
     6: Workload(6, "varlen_causal_bf16", B=1, Hq=32, Hkv=8, N=32768, d=128, dtype="bf16",
                 mask=MASK_CAUSAL | MASK_DOC, extra={"varlen": True, "len_range": (128, 4096)}),
