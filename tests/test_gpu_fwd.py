@@ -53,6 +53,8 @@ SMALL = [
     ("causal d128", I.WORKLOADS[2].shrink(B=2, Hq=3, Hkv=3, N=1000), None),
     # 16 heads of 4 query tiles: the grid is dispatched two heads per XCD at a time
     ("causal 16 heads grouped", I.WORKLOADS[2].shrink(B=2, Hq=8, Hkv=8, N=1000), None),
+    # grouped order with GQA: 8 key / value heads, their query heads placed 8 slots apart
+    ("gqa 32 heads grouped", I.WORKLOADS[2].shrink(B=2, Hq=16, Hkv=4, N=900), None),
     ("dense d128", I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=777, mask=0), None),
     ("causal d64", I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=600, d=64), None),
     ("dense d64", I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=333, d=64, mask=0), None),

@@ -31,7 +31,8 @@ struct BwdParams {
     int B, Hq, Hkv, G, N;
     float scale, scale_log2;
     int causal;
-    int xg_kv, xg_q;   // heads per XCD dispatch group of the dK/dV and dQ grids, 0 = plain order
+    int xg_kv, xg_q;   // heads per XCD dispatch group of the dK/dV and dQ parts, 0 = plain order
+    int n_kv;          // dK/dV workgroups of the gradient grid (a multiple of 8), the dQ ones follow
 };
 
 // Work item of a grid of n_heads x ng workgroups, group index heaviest first
@@ -171,7 +172,7 @@ __device__ __forceinline__ void store_rows(__bf16* head, int r0, int N, int lane
 // reloaded from scratch per chunk) hide the latency of each wave's serial
 // chain S -> P -> dV, dK about 1.35x better than one wave per SIMD with
 // everything in registers.
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid) {
     __shared__ __attribute__((aligned(1024))) char lds[2][2][kBC * Tile<kBD>::ROW_BYTES];   // buffer, Q / dO
     __shared__ __attribute__((aligned(16))) float stat[2][2 * kBC];   // buffer: LSE then D of the chunk
     const int lane = threadIdx.x & 63;
@@ -179,7 +180,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int nkb = (p.N + kBC - 1) / kBC, nkg = (nkb + 3) / 4;
     // heavy groups first: under a causal mask the first key blocks see the most query chunks
     int kg, bg;
-    grid_item(blockIdx.x, p.B * p.Hkv, nkg, p.xg_kv, bg, kg);
+    if (bid >= p.B * p.Hkv * nkg) return;   // padding of the dK/dV part to a multiple of 8
+    grid_item(bid, p.B * p.Hkv, nkg, p.xg_kv, bg, kg);
     const int g = bg % p.Hkv, b = bg / p.Hkv;
     const int kb = 4 * kg + wave;   // may be >= nkb: then every key of the block is masked
     const int l32 = lane & 31, hh = lane >> 5;
@@ -258,14 +260,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 // last query block still copies and meets the barriers, and stores nothing);
 // under a causal mask the group runs to the last chunk its last block sees,
 // the chunks beyond a block's diagonal being fully masked (exact zeros).
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_block(const BwdParams& p, int bid) {
     __shared__ __attribute__((aligned(1024))) char lds[2][2][kBC * Tile<kBD>::ROW_BYTES];   // buffer, K / V
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nqb = (p.N + kBC - 1) / kBC, nqg = (nqb + 3) / 4;
     // heavy groups first: under a causal mask the last query blocks see the most key chunks
     int qg, bh;
-    grid_item(blockIdx.x, p.B * p.Hq, nqg, p.xg_q, bh, qg);
+    grid_item(bid, p.B * p.Hq, nqg, p.xg_q, bh, qg);
     qg = nqg - 1 - qg;
     const int h = bh % p.Hq, b = bh / p.Hq;
     const int qb = 4 * qg + wave;   // may be >= nqb: then every query of the block is masked
@@ -330,6 +332,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     store_rows(p.dq + qh * kBD, i0, p.N, lane, dq, p.scale);
 }
 
+// dK/dV and dQ need only the inputs and D, not each other: one grid holds the
+// dK/dV workgroups first and the dQ workgroups after them, so the dQ work
+// fills the CUs the end of the dK/dV part leaves idle. Two workgroups per CU
+// (two waves per SIMD, 256 registers each: dK/dV reloads a few values from
+// scratch per chunk) hide the latency of each wave's serial product chain.
+// The dK/dV part is padded to a multiple of 8 workgroups, so that workgroup
+// n_kv + w of the dQ part runs on the XCD w would (round-robin dispatch).
+__global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
+    const int bid = blockIdx.x;
+    if (bid < p.n_kv) dkdv_block(p, bid);
+    else dq_block(p, bid - p.n_kv);
+}
+
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, float scale,
                       int causal, hipStream_t st) {
@@ -357,10 +372,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     };
     p.xg_kv = xcd_group((long long)p.B * p.Hkv);
     p.xg_q = xcd_group((long long)p.B * p.Hq);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((long long)p.B * p.Hkv * ng)), dim3(256), 0, st, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((long long)p.B * p.Hq * ng)), dim3(256), 0, st, p);
+    const long long n_kv = ((long long)p.B * p.Hkv * ng + 7) / 8 * 8;
+    p.n_kv = (int)n_kv;
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(n_kv + (long long)p.B * p.Hq * ng)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
