@@ -22,10 +22,12 @@ CASES = [
     (3, 4, 2, [31, 32, 65], 8),
     # equal and empty lengths: the sequences are launched longest first, ties by index
     (9, 4, 2, [50, 300, 50, 0, 300, 7, 1000, 50, 0], 4),
+    (70, 4, 2, [(i * 37) % 50 * 7 for i in range(70)], 3),
 ]
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,lens,splits", CASES, ids=[f"{c[1]}x{c[2]}-{c[3]}-s{c[4]}" for c in CASES])
+@pytest.mark.parametrize("B,Hq,Hkv,lens,splits", CASES,
+                         ids=[f"B{c[0]}-{c[1]}x{c[2]}-{c[3][:4]}-s{c[4]}" for c in CASES])
 def test_decode_matches_oracle(B, Hq, Hkv, lens, splits):
     print(f"[case] decode B={B} Hq={Hq} Hkv={Hkv} lens={lens} splits={splits}", flush=True)
     q, kc, vc, bt, sl = I.decode_inputs(B, Hq, Hkv, 128, lens, seed=sum(lens) + splits)
