@@ -600,14 +600,15 @@ static hipError_t launch_bf16_inst(const FwdParams& p0, hipStream_t st) {
     constexpr int BM = 256;
     p.n_qt = (p.Nq + BM - 1) / BM;
     p.n_bh = p.B * p.Hq;
-    // Head groups per XCD: as many heads as fill its resident workgroups
-    // (32 CUs, one workgroup each), when the heads split evenly over the 8
-    // XCDs and into groups of at least two. With one head per group (long
-    // sequences) the plain order measured faster.
+    // Head groups per XCD: as many heads as fill two rounds of its resident
+    // workgroups (32 CUs, one workgroup each; one round measured slower),
+    // when the heads split evenly over the 8 XCDs and into groups of at
+    // least two. With one head per group (long sequences) the plain order
+    // measured faster.
     p.xgrp = 0;
     if (p.n_bh % 8 == 0) {
         const int per_xcd = p.n_bh / 8;
-        int g = 32 / p.n_qt;
+        int g = 64 / p.n_qt;
         while (g > 1 && per_xcd % g) --g;
         p.xgrp = g >= 2 ? g : 0;
     }
