@@ -307,7 +307,9 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms_prep = e0.elapsed_time(e1) / 10
-        prep_bytes = 2 * (q.numel() + k.numel() + v.numel()) + q8.numel() + k8.numel() + v8.numel()
+        # read Q, K, V (bf16); write value + residual codes of Q and K, V's codes, the scales
+        v_plane = w.B * w.Hkv * (-(-w.N // 128) * 128) * w.d   # V's unused residual plane
+        prep_bytes = 2 * (q.numel() + k.numel() + v.numel()) + q8.numel() + k8.numel() + v8.numel() - v_plane
         # the same step with the rotary embedding of Q and K fused in front
         rc, rs = (t.to("cuda") for t in I.rope_tables(w.N, w.d))
         for _ in range(2):

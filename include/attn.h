@@ -137,15 +137,22 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  * outliers before fp8 quantisation).
  *
  * Packed buffer format (one per tensor), for H heads and N tokens, with
- * Np = N rounded up to a multiple of 128:
- *   bytes [0, B*H*Np*d)        e4m3 (OCP, max 448) codes;
- *                              Q and K: [B][H][Np][d] (rows rotated: x D H);
- *                              V:       [B][H][d][Np] (transposed, not rotated);
- *                              padding rows / columns hold 0.
- *   then, at byte offset B*H*Np*d, float32 scales [B][H][Np/128]: one per
- *   tile of 128 tokens of one head; value = scale * code (scale = tile
- *   amax / 448, 1 for an all-zero tile); codes are rounded to nearest even
- *   and saturate at +-448.
+ * Np = N rounded up to a multiple of 128 and P = B*H*Np*d (one code plane):
+ *   bytes [0, P)       e4m3 (OCP, max 448) value codes c1;
+ *                      Q and K: [B][H][Np][d] (rows rotated: x D H);
+ *                      V:       [B][H][d][Np] (transposed, not rotated);
+ *                      padding rows / columns hold 0.
+ *   bytes [P, 2P)      Q and K only: e4m3 residual codes c2, same layout;
+ *                      c2 = e4m3(x / scale - value(c1)) on the same scale, so
+ *                      x ~ scale * (value(c1) + value(c2)) to about 2^-7
+ *                      relative. Not read or written for V.
+ *   then, at byte offset 2P, float32 scales [B][H][Np/128]: one per tile of
+ *   128 tokens of one head (scale = tile amax / 448, 1 for an all-zero
+ *   tile); codes are rounded to nearest even and c1 saturates at +-448.
+ * The forward scores a (query, key) pair with the three products
+ * c1.c1' + c1.c2' + c2.c1' of its rows (the c2.c2' term is left out): one
+ * e4m3 code alone misses the 5e-2 relative-RMS accuracy bar on inputs with
+ * x20 outlier channels (the rounding error of Q and K dominates there).
  * attn_fp8_buffer_bytes gives the size of one such buffer (0 on bad sizes).
  *
  * q, k, v : device bfloat16 BHSD inputs, Q [B][Hq][N][d], K/V [B][Hkv][N][d].

@@ -108,6 +108,25 @@ def quantize_rows(x, tile=SCALE_TILE):
     return codes, scales
 
 
+def quantize_rows_split(x, tile=SCALE_TILE):
+    """Two e4m3 codes per element sharing the tile scale of ``quantize_rows``.
+
+    code1 = e4m3(x / scale) and code2 = e4m3(x / scale - value(code1)): the
+    residual of the first rounding, rounded again on the same scale, so that
+    value(code1) + value(code2) carries about 2 x 3 mantissa bits. Returns
+    (code1, code2, scales). Not on the page: an e4m3 expansion of the rotated
+    Q and K, taken because a single code misses the fp8 accuracy bar on
+    inputs with outlier channels.
+    """
+    c1, sc = quantize_rows(x, tile)
+    x = np.asarray(x, dtype=np.float64)
+    N = x.shape[2]
+    rep = np.repeat(sc.astype(np.float64), tile, axis=2)[:, :, :N, None]
+    t = np.clip(x / rep, -E4M3_MAX, E4M3_MAX)
+    c2 = e4m3_code(t - e4m3_value(c1))
+    return c1, c2, sc
+
+
 def dequantize_rows(codes, scales, tile=SCALE_TILE):
     """Inverse of ``quantize_rows``: value(code) * scale, float64."""
     v = e4m3_value(codes)
@@ -145,7 +164,9 @@ def prepare(q, k, v, signs, tile=SCALE_TILE, rope_cos=None, rope_sin=None):
     """The fp8 prepare step: (optionally RoPE, then) rotate Q and K, then
     quantise Q, K, V per tile.
 
-    Returns dict with the rotated float64 inputs and the (codes, scales) triples.
+    Returns a dict with the rotated float64 inputs, (codes, scales) pairs for
+    Q, K and V, and (value codes, residual codes, scales) for Q and K under
+    "q_split" / "k_split".
     """
     if rope_cos is not None:
         q = rope(q, rope_cos, rope_sin)
@@ -156,20 +177,25 @@ def prepare(q, k, v, signs, tile=SCALE_TILE, rope_cos=None, rope_sin=None):
     return {
         "q_rot": qr, "k_rot": kr,
         "q": quantize_rows(qr, tile), "k": quantize_rows(kr, tile), "v": quantize_rows(vv, tile),
+        "q_split": quantize_rows_split(qr, tile), "k_split": quantize_rows_split(kr, tile),
     }
 
 
 def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=4, rotate_qk=True,
-                       tile=SCALE_TILE, heads=None, lazy_tau=None):
+                       tile=SCALE_TILE, heads=None, lazy_tau=None, qk_codes=2):
     """fp8 emulation of the whole path, float64 arithmetic (no mask).
 
     Q, K (rotated when ``rotate_qk``) and V are quantised per tile of ``tile``
-    tokens; scores are exact on the dequantised Q, K. The online softmax walks
-    key blocks of ``block_n`` with the exact running max m; each block's
-    probabilities p = exp(s - m) are stored as e4m3(p * 2^p_shift * s_v / s_vmax)
-    (s_v: the V scale of the block's tile, s_vmax: the largest V scale of the
-    head) and multiply the V codes; the running sum uses the unrounded p; the
-    output is rescaled by s_vmax / 2^p_shift at the end.
+    tokens. With ``qk_codes`` = 2, Q and K carry a value code and a residual
+    code on one scale (``quantize_rows_split``) and a score is the sum of the
+    three products value.value + value.residual + residual.value (the
+    residual.residual term, below 2^-8 of the score, is left out); with 1,
+    value codes only. The online softmax walks key blocks of ``block_n``:
+    running max m; each block's probabilities p = exp(s - m) are stored as
+    e4m3(p * 2^p_shift * s_v / s_vmax) (s_v: the V scale of the block's tile,
+    s_vmax: the largest V scale of the head) and multiply the V codes; the
+    running sum uses the unrounded p; the output is rescaled by
+    s_vmax / 2^p_shift at the end.
 
     ``lazy_tau`` (natural-log units) selects the other valid reference schedule:
     the exponent reference is moved to the running max only when that max has
@@ -183,8 +209,16 @@ def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=4, rotate_qk=T
     v = np.asarray(v, dtype=np.float64)
     if rotate_qk:
         q, k = rotate(q, signs), rotate(k, signs)
-    qd = dequantize_rows(*quantize_rows(q, tile), tile)
-    kd = dequantize_rows(*quantize_rows(k, tile), tile)
+    if qk_codes == 2:
+        q1, q2, qs = quantize_rows_split(q, tile)
+        k1, k2, ks = quantize_rows_split(k, tile)
+        qa, qb = dequantize_rows(q1, qs, tile), dequantize_rows(q2, qs, tile)
+        ka, kb = dequantize_rows(k1, ks, tile), dequantize_rows(k2, ks, tile)
+    elif qk_codes == 1:
+        qa, ka = dequantize_rows(*quantize_rows(q, tile), tile), dequantize_rows(*quantize_rows(k, tile), tile)
+        qb, kb = np.zeros_like(qa), np.zeros_like(ka)
+    else:
+        raise ValueError("qk_codes must be 1 or 2")
     vc, vs = quantize_rows(v, tile)
     v8 = e4m3_value(vc)
     B, Hq, N, d = q.shape
@@ -201,7 +235,7 @@ def attention_emulated(q, k, v, signs, scale, block_n=64, p_shift=4, rotate_qk=T
         acc = np.zeros((N, d))
         for j0 in range(0, Nk, block_n):
             cols = slice(j0, min(j0 + block_n, Nk))
-            s = scale * (qd[b, h] @ kd[b, g, cols].T)
+            s = scale * (qa[b, h] @ ka[b, g, cols].T + qa[b, h] @ kb[b, g, cols].T + qb[b, h] @ ka[b, g, cols].T)
             m_new = np.maximum(m, s.max(axis=1))
             if lazy_tau is not None:
                 m_new = np.where(np.isfinite(m) & (m_new <= m + lazy_tau), m, m_new)

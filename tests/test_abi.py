@@ -115,8 +115,9 @@ def test_fwd_varlen_rejects_unsupported(lib, kw):
 
 
 def test_fp8_buffer_bytes(lib):
-    # 300 tokens -> 384 padded rows of 128 bytes, 3 float32 scales per head
-    assert _lib.attn_fp8_buffer_bytes(2, 3, 300, 128) == 2 * 3 * 384 * 128 + 2 * 3 * 3 * 4
+    # 300 tokens -> 384 padded rows of 128 bytes in two code planes (value,
+    # residual), 3 float32 scales per head
+    assert _lib.attn_fp8_buffer_bytes(2, 3, 300, 128) == 2 * (2 * 3 * 384 * 128) + 2 * 3 * 3 * 4
     assert _lib.attn_fp8_buffer_bytes(0, 3, 300, 128) == 0
 
 

@@ -2,12 +2,14 @@
 
 The prepare step is checked element by element: every stored scale equals the
 tile amax / 448 of the oracle's float64 rotation (float32 rounding), and every
-code is a correct e4m3 rounding of oracle_value / scale (the codes equal the
-oracle's round-to-nearest-even except where float32 and float64 rotations fall
-on opposite sides of a rounding midpoint, which the check allows). The fp8
-forward is compared with the fp8 emulation (same quantisation scheme, float64
-arithmetic; relative RMS <= 1e-2) and with the exact float64 attention on the
-unquantised inputs (relative RMS reported per head).
+value and residual code is a correct e4m3 rounding of its oracle target (the
+codes equal the oracle's round-to-nearest-even except where float32 and
+float64 rotations fall on opposite sides of a rounding midpoint, which the
+check allows). The fp8 forward is held to the accuracy bar, relative RMS
+<= 5e-2 against the exact float64 attention on the unquantised inputs, over
+the whole output and on every head, at the full workload size; it is also
+compared with the fp8 emulation (same quantisation scheme, float64
+arithmetic, pinned against a pure-Python brute force on the CPU).
 """
 import numpy as np
 import pytest
@@ -19,6 +21,8 @@ from tiled_attention_05_amd import _lib
 from tiled_attention_05_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
+
+FP8_RELRMS = 5e-2   # relative RMS of O against the exact float64 attention on the unquantised inputs
 
 
 def _half_step(t):
@@ -58,6 +62,33 @@ def _check_codes(codes_gpu, scales_gpu, x64, tile=128, tie_abs=1e-12):
     return float(np.mean(exact)), float(np.mean(tie))
 
 
+def _check_residual(res_gpu, codes_gpu, scales_gpu, x64, tile=128, rel=1e-5, tie_abs=1e-4):
+    """Residual codes: e4m3 of (x / scale - value(code)) on the same scale. The
+    kernel forms x / scale in float32 after a float32 Walsh-Hadamard transform
+    (sums of 128 terms), so x / scale carries an error of about 1e-5 of its
+    size (the value-code check allows the same); the residual inherits that
+    error in full. Near a midpoint of the residual's grid, within that error,
+    either neighbour is accepted; everywhere the pair must be within half a
+    residual step (plus that error) of x / scale."""
+    B, H, N, d = x64.shape
+    sc = np.repeat(scales_gpu.astype(np.float64), tile, axis=2)[:, :, :N, None]
+    t = np.clip(x64 / sc, -448.0, 448.0)
+    r = t - F8.e4m3_value(codes_gpu)
+    dec = F8.e4m3_value(res_gpu)
+    slack = rel * np.abs(t) + tie_abs
+    assert np.all(np.abs(dec - r) <= _half_step(r) * (1 + 1e-3) + slack), "residual code out of bounds"
+    exact = res_gpu == F8.e4m3_code(r)
+    a = np.abs(r)
+    i = np.clip(np.searchsorted(_MIDS, a), 1, len(_MIDS) - 1)
+    tie = np.minimum(np.abs(a - _MIDS[i]), np.abs(a - _MIDS[i - 1])) <= slack
+    bad = ~exact & ~tie
+    if bad.any():
+        print(f"[fp8-prepare] residual mismatches (t, r, gpu, float64): "
+              f"{list(zip(t[bad][:4], r[bad][:4], dec[bad][:4], F8.e4m3_round(r[bad][:4])))}", flush=True)
+    assert not bad.any(), f"{np.sum(bad)} residual codes differ away from a midpoint"
+    return float(np.mean(exact))
+
+
 def _relrms(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
@@ -93,6 +124,11 @@ def test_prepare_matches_oracle(N, Hq, Hkv):
         assert np.all(codes[:, :, N:] == 0), f"{name}: padding must hold zeros"
         print(f"[fp8-prepare] {name}: codes equal to float64 RNE: {same:.6f} (midpoint ties {ties:.6f})",
               flush=True)
+        if not tr:
+            res = _lib.fp8_unpack_residual(buf, w.B, H, N, 128).cpu().numpy()
+            rsame = _check_residual(res[:, :, :N], codes[:, :, :N], scales, xr)
+            assert np.all(res[:, :, N:] == 0), f"{name}: residual padding must hold zeros"
+            print(f"[fp8-prepare] {name}: residual codes equal to float64 RNE: {rsame:.6f}", flush=True)
 
 
 def _pack_oracle(w, x):
@@ -104,11 +140,12 @@ def _pack_oracle(w, x):
     those codes separately."""
     signs = x["signs"].numpy()
     q64, k64, v64 = (x[n].double().numpy() for n in ("q", "k", "v"))
-    parts = [(F8.quantize_rows(F8.rotate(q64, signs)), w.Hq, False),
-             (F8.quantize_rows(F8.rotate(k64, signs)), w.Hkv, False),
-             (F8.quantize_rows(v64), w.Hkv, True)]
+    vc, vs = F8.quantize_rows(v64)
+    parts = [(F8.quantize_rows_split(F8.rotate(q64, signs)), w.Hq, False),
+             (F8.quantize_rows_split(F8.rotate(k64, signs)), w.Hkv, False),
+             ((vc, None, vs), w.Hkv, True)]
     bufs = []
-    for (codes, scales), H, tr in parts:
+    for (codes, resid, scales), H, tr in parts:
         buf = torch.zeros(_lib.attn_fp8_buffer_bytes(w.B, H, w.N, w.d), dtype=torch.uint8)
         cv, sv = _lib.fp8_unpack(buf, w.B, H, w.N, w.d, transposed=tr)
         c = torch.from_numpy(codes)
@@ -116,6 +153,7 @@ def _pack_oracle(w, x):
             cv[:, :, :, :w.N] = c.transpose(2, 3)
         else:
             cv[:, :, :w.N] = c
+            _lib.fp8_unpack_residual(buf, w.B, H, w.N, w.d)[:, :, :w.N] = torch.from_numpy(resid)
         sv.copy_(torch.from_numpy(scales))
         bufs.append(buf.cuda())
     return bufs
@@ -143,41 +181,42 @@ def test_fp8_forward_small(N, Hq, Hkv):
           f"lse vs exact {np.abs(lg - L).max():.3e}", flush=True)
     assert r_emu <= 1e-2
     assert np.abs(lg - Le).max() <= 1e-3
-    assert r_exact <= r_scheme + 1e-2
+    assert r_exact <= FP8_RELRMS
 
 
-def test_fp8_workload_sampled_heads():
+
+def test_fp8_workload_all_heads():
+    """The whole fp8 workload (B=4, H=16, N=8192, d=128, two x20 outlier channels in
+    Q and in K): prepare + forward against the exact float64 attention of all 64
+    heads, relative RMS <= 5e-2 over the whole output and on every head."""
     w = I.WORKLOADS[5]
-    print("[case] fp8 workload, sampled heads", flush=True)
+    print("[case] fp8 workload, all 64 heads against the float64 oracle", flush=True)
     x, (q8, k8, v8) = _prep(w)
     o, lse = _lib.fwd_fp8(q8, k8, v8, w.B, w.Hq, w.Hkv, w.N, 128, scale=w.scale)
     torch.cuda.synchronize()
-    # heads with an outlier channel in Q or K, and plain ones
-    base = I.qkv(w, outliers="none")
-    big_q = ((x["q"].float() / base[0].float()).abs() > 10).any(dim=2).any(dim=0).any(dim=1)
-    big_k = ((x["k"].float() / base[1].float()).abs() > 10).any(dim=2).any(dim=0).any(dim=1)
-    hot = sorted(set(torch.nonzero(big_q | big_k).flatten().tolist()))
-    cold = [h for h in range(w.Hq) if h not in hot][:2]
-    heads = [(0, h) for h in hot[:2] + cold]
-    O, L = A.attention(x["q"], x["k"], x["v"], w.scale, heads=heads)
-    og = torch.stack([o[b, h] for b, h in heads]).float().cpu().double().numpy()
-    lg = torch.stack([lse[b, h] for b, h in heads]).cpu().double().numpy()
-    per = {h: _relrms(og[i], O[i]) for i, (_, h) in enumerate(heads)}
-    tot = _relrms(og, O)
-    print(f"[fp8-workload] relRMS per head {per}; outlier heads {hot}; all sampled {tot:.4f}; "
-          f"lse max err {np.abs(lg - L).max():.3e}", flush=True)
-    assert tot <= 0.15
+    og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    del o, lse, q8, k8, v8
+    O, L = A.attention(x["q"], x["k"], x["v"], w.scale)
     assert np.isfinite(og).all()
+    tot = _relrms(og, O)
+    num = np.sqrt(((og - O) ** 2).sum(axis=(2, 3)))
+    per = num / np.sqrt((O ** 2).sum(axis=(2, 3)))
+    worst = np.unravel_index(np.argmax(per), per.shape)
+    print(f"[fp8-workload] relRMS whole output {tot:.4f}; per head max {per.max():.4f} at (b, h) = {worst}, "
+          f"median {np.median(per):.4f}; lse max err {np.abs(lg - L).max():.3e}", flush=True)
+    assert tot <= FP8_RELRMS
+    assert per.max() <= FP8_RELRMS
 
 
 @pytest.mark.parametrize("outliers", ["channels", "entries"])
 def test_hadamard_on_off_error_ratio(outliers):
     """Reports the fp8 error with and without the random-sign Hadamard rotation
-    (the page reports 2.6x lower error with it, on outlier entries). The ratio
-    is a measurement, not a bar: with per-tile scales and x20 outliers no value
-    falls into e4m3's subnormal range, so rounding error stays relative per
-    element with or without the rotation. Both variants must stay finite and
-    within the fp8 error scale."""
+    (the page reports 2.6x lower error with it, for one fp8 code per element, on
+    outlier entries). The ratio is a measurement, not a bar: with value +
+    residual codes the Q / K rounding error is small either way, and with
+    per-tile scales and x20 outliers no value falls into e4m3's subnormal
+    range. Both variants must stay finite and within the fp8 bar."""
     w = I.WORKLOADS[5].shrink(B=1, Hq=4, Hkv=4, N=1024)
     errs = {}
     for rot in (True, False):
@@ -189,7 +228,7 @@ def test_hadamard_on_off_error_ratio(outliers):
     ratio = errs[False] / errs[True]
     print(f"[fp8-hadamard] {outliers}: relRMS rotated {errs[True]:.4f}, plain {errs[False]:.4f}, "
           f"ratio plain/rotated {ratio:.2f}", flush=True)
-    assert all(np.isfinite(e) and e < 0.25 for e in errs.values())
+    assert all(np.isfinite(e) and e <= FP8_RELRMS for e in errs.values())
 
 
 def _rope_tables(N, d):

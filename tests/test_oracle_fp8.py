@@ -124,10 +124,15 @@ def test_emulation_error_is_bounded_and_hadamard_helps():
     O, _ = A.attention(q, k, v, scale)
     O = O.reshape(B * H, N, d)
     rel = lambda X: np.linalg.norm(X - O) / np.linalg.norm(O)
-    Oh, _ = F8.attention_emulated(q, k, v, signs, scale, rotate_qk=True)
-    On, _ = F8.attention_emulated(q, k, v, signs, scale, rotate_qk=False)
+    # the page's setting: one e4m3 code per element of Q and K
+    Oh, _ = F8.attention_emulated(q, k, v, signs, scale, rotate_qk=True, qk_codes=1)
+    On, _ = F8.attention_emulated(q, k, v, signs, scale, rotate_qk=False, qk_codes=1)
     assert rel(Oh) < 0.1
     assert rel(On) / rel(Oh) > 1.2
+    # value + residual codes remove most of the Q / K rounding error: what is left
+    # is V's codes and P's rounding (each about 2^-4 / sqrt(3) * 0.7 relative)
+    O2, _ = F8.attention_emulated(q, k, v, signs, scale, rotate_qk=True, qk_codes=2)
+    assert rel(O2) < 0.05 and rel(O2) < 0.8 * rel(Oh)
 
 
 def test_emulation_with_identity_codec_equals_exact():
@@ -144,3 +149,66 @@ def test_emulation_with_identity_codec_equals_exact():
     Oe, Le = F8.attention_emulated(q, k, v, np.ones(128), 0.1, rotate_qk=False, block_n=16)
     np.testing.assert_allclose(Le, L.reshape(1, 64), atol=1e-12)
     np.testing.assert_allclose(Oe, O.reshape(1, 64, 128), atol=0.02 * np.abs(v).max())
+
+
+def test_split_codes_residual_and_error():
+    """value + residual codes on one tile scale: the residual is the rounding error
+    of the value code rounded again, so the pair's error is the residual's own
+    rounding error, at most half an e4m3 step of the residual (<= 2^-4 of it,
+    or 2^-10 on the subnormal grid) -- about 2^-8 of the element instead of 2^-4."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((2, 2, 260, 32)) * rng.uniform(0.1, 10, (2, 2, 1, 1))
+    x[0, 1, 5, 3] *= 20.0
+    c1, c2, sc = F8.quantize_rows_split(x)
+    c1b, scb = F8.quantize_rows(x)
+    np.testing.assert_array_equal(c1, c1b)
+    np.testing.assert_array_equal(sc, scb)
+    rep = np.repeat(sc.astype(np.float64), 128, axis=2)[:, :, :260, None]
+    t = x / rep
+    r = t - F8.e4m3_value(c1)
+    err = np.abs(F8.e4m3_value(c1) + F8.e4m3_value(c2) - t)
+    assert np.all(err <= np.maximum(np.abs(r) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-9))
+    # the residual never needs more than the value code's half step: |c2| <= 16 < 448
+    assert np.abs(F8.e4m3_value(c2)).max() <= 16.0
+    big = np.abs(t) > 1.0
+    assert np.median(err[big] / np.abs(t[big])) < 2.0 ** -8
+
+
+@pytest.mark.parametrize("split,tau,rotate", [(True, None, True), (True, 4 * np.log(2), True),
+                                              (False, 4 * np.log(2), True), (True, None, False)])
+def test_emulation_matches_brute_force(split, tau, rotate):
+    """The fp8 emulation (numpy) against an independent pure-Python brute force of
+    the same scheme (tests/brute_fp8.py: e4m3 rounding by exponent and step, the
+    closed-form Hadamard, per-element loops): rotation, tile scales, value and
+    residual codes, the reference schedule and the rounding of P all agree."""
+    from tests import brute_fp8 as BF
+    rng = np.random.default_rng(23)
+    N, d, tile, block = 22, 8, 8, 4
+    q = rng.standard_normal((1, 1, N, d)) * 2
+    k = rng.standard_normal((1, 1, N, d)) * 2
+    v = rng.standard_normal((1, 1, N, d))
+    q[..., 3] *= 20.0
+    v[0, 0, 9] *= 20.0                      # an outlier V token: its tile has the largest scale
+    signs = rng.integers(0, 2, d) * 2 - 1
+    scale = 0.7
+    Oe, Le = F8.attention_emulated(q, k, v, signs, scale, block_n=block, tile=tile, lazy_tau=tau,
+                                   qk_codes=2 if split else 1, rotate_qk=rotate)
+    Ob, Lb = BF.attend_fp8(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), [float(x) for x in signs],
+                           scale, tile, block, tau=tau, split=split, rotate=rotate)
+    np.testing.assert_allclose(Oe[0], np.array(Ob), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(Le[0], np.array(Lb), rtol=0, atol=1e-12)
+    # and the scheme differs from the exact result by an fp8-sized amount, not 0
+    O, _ = A.attention(q, k, v, scale)
+    assert np.abs(Oe[0] - O[0, 0]).max() > 1e-4
+
+
+def test_brute_force_e4m3_matches_codec():
+    """The brute force's rounding equals the oracle codec on every code, every
+    midpoint and points around them (so the brute-force pin is not vacuous)."""
+    from tests import brute_fp8 as BF
+    vals = F8.e4m3_value(np.arange(0x7F))
+    mids = (vals[1:] + vals[:-1]) / 2
+    pts = np.concatenate([vals, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+                          np.random.default_rng(2).uniform(-500, 500, 2000)])
+    ours = np.array([BF.e4m3(float(x)) for x in pts])
+    np.testing.assert_array_equal(ours, F8.e4m3_round(pts))

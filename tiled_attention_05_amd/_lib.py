@@ -302,12 +302,19 @@ def fwd_fp8(q8, k8, v8, B, Hq, Hkv, N, d, scale=None, with_lse=True, stream=None
 
 
 def fp8_unpack(buf, B, H, N, d, transposed=False):
-    """Views of a packed fp8 buffer: (codes uint8, scales float32)."""
+    """Views of a packed fp8 buffer: (value codes uint8, scales float32)."""
     npad = (N + FP8_TILE - 1) // FP8_TILE * FP8_TILE
     n = B * H * npad * d
     codes = buf[:n].view(B, H, d, npad) if transposed else buf[:n].view(B, H, npad, d)
-    scales = buf[n:n + B * H * (npad // FP8_TILE) * 4].view(torch.float32).view(B, H, npad // FP8_TILE)
+    scales = buf[2 * n:2 * n + B * H * (npad // FP8_TILE) * 4].view(torch.float32).view(B, H, npad // FP8_TILE)
     return codes, scales
+
+
+def fp8_unpack_residual(buf, B, H, N, d):
+    """View of the residual codes (uint8 [B, H, Np, d]) of a packed Q or K buffer."""
+    npad = (N + FP8_TILE - 1) // FP8_TILE * FP8_TILE
+    n = B * H * npad * d
+    return buf[n:2 * n].view(B, H, npad, d)
 
 
 def block_mask(B, Nq, Nk, mask, window=0, doc_ids=None, block_m=128, block_n=64, device="cuda",

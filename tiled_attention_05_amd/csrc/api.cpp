@@ -161,8 +161,8 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 size_t attn_fp8_buffer_bytes(int B, int H, int N, int d) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
     const size_t np = (size_t)(N + kFp8Tile - 1) / kFp8Tile * kFp8Tile;
-    const size_t data = (size_t)B * H * np * d;
-    return data + (size_t)B * H * (np / kFp8Tile) * sizeof(float);
+    const size_t plane = (size_t)B * H * np * d;   // value codes, then residual codes
+    return 2 * plane + (size_t)B * H * (np / kFp8Tile) * sizeof(float);
 }
 
 int attn_fp8_prepare(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N, int d,

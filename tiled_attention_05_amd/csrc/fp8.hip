@@ -34,8 +34,12 @@ constexpr float kFp8PShift = 4.f;    // P is stored as e4m3(p * 2^4 * s_v / s_vm
 // on different bits commute, so their order does not change the result. Then
 // the tile's amax gives scale = amax / 448 and the codes are the round-to-
 // nearest-even e4m3 values of x / scale (clamped to +-448 first, so nothing
-// saturates to NaN). V is not rotated and is written transposed, [d][tokens],
-// so the attention kernel reads contiguous keys per lane.
+// saturates to NaN). Q and K also get a residual code on the same scale,
+// e4m3(x / scale - value(code)): the difference is exact in float32 (the code
+// is within a factor 17/16 of x / scale), so value + residual carries about
+// six mantissa bits. V is not rotated, has one code and is written
+// transposed, [d][tokens], so the attention kernel reads contiguous keys per
+// lane.
 // With rotary tables (rope_cos / rope_sin, float32 [N][d/2]) Q and K rows are
 // first turned pairwise, (x_i, x_{i+d/2}) by the token's angle (the pair sits
 // in one lane: j and j + 2): both passes are memory-bound over the same rows,
@@ -180,7 +184,8 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(const __bf16* __restri
     am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = am > 0.f ? am / kE4m3Max : 1.f;
     const float inv = 1.f / sc;
-    float* scales = (float*)(dst + (size_t)B * H * Np * D);
+    const size_t plane = (size_t)B * H * Np * D;   // bytes of one code plane
+    float* scales = (float*)(dst + 2 * plane);
     if (threadIdx.x == 0) scales[(size_t)bh * nt + tile] = sc;
 
 #pragma unroll
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(const __bf16* __restri
         const int row = tile * kFp8Tile + t;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t w2[2];
+            uint32_t w2[2], r2[2];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const float* z = x[it][j] + 4 * h2;
@@ -200,9 +205,18 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(const __bf16* __restri
                 int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
                 pk = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, pk, true);
                 w2[h2] = (uint32_t)pk;
+                if (which < 2) {   // residual of the rounding, on the same scale
+                    const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+                    const auto v23 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+                    int rk = __builtin_amdgcn_cvt_pk_fp8_f32(a0 - v01[0], a1 - v01[1], 0, false);
+                    rk = __builtin_amdgcn_cvt_pk_fp8_f32(a2 - v23[0], a3 - v23[1], rk, true);
+                    r2[h2] = (uint32_t)rk;
+                }
             }
             if (which < 2) {
-                *(uint2*)(dst + ((size_t)bh * Np + row) * D + 8 * c + 32 * j) = make_uint2(w2[0], w2[1]);
+                uint8_t* rp = dst + ((size_t)bh * Np + row) * D + 8 * c + 32 * j;
+                *(uint2*)rp = make_uint2(w2[0], w2[1]);
+                *(uint2*)(rp + plane) = make_uint2(r2[0], r2[1]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) vt[8 * c + 32 * j + e][t] = (uint8_t)(w2[e >> 2] >> (8 * (e & 3)));
@@ -237,7 +251,11 @@ hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B
 // -----------------------------------------------------------------------------
 // fp8 forward, d = 128, no mask. Same tiling and two-waves-per-SIMD ping-pong
 // as the bf16 kernel (see attn_fwd_bf16.hip), on 32x32x64 e4m3 matrix cores:
-//   GEMM0  S^T = K8 Q8^T   per 64-key tile: 2 key blocks x 2 k-steps of 64.
+//   GEMM0  S^T = K8 Q8^T   per 64-key tile: 2 key blocks x 2 k-steps of 64,
+//          three products per step on one accumulator: value x value,
+//          value(K) x residual(Q) and residual(K) x value(Q) (the residual x
+//          residual term, below 2^-8 of the score, is left out); both codes
+//          of a row share its tile scale, so the sum is one scaled score.
 //          The K rows of block kb are read in the order
 //              pi(m) = 32 ((m >> 2) & 1) + 16 kb + 4 (m >> 3) + (m & 3)
 //          so that accumulator register r of half-wave h holds key
@@ -265,7 +283,9 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     constexpr int NW = 8, BM = NW * 32, D = 128;
     constexpr int PF = 2, NKB = PF + 1, NVB = PF + 2;
     constexpr float kTau = kFp8PShift;   // lazy-rescale threshold (log2 units)
-    __shared__ __attribute__((aligned(1024))) char tiles_lds[NKB * T::KBYTES + NVB * T::VBYTES];
+    constexpr int KBUF = 2 * T::KBYTES;  // key tile: value codes, then residual codes
+    constexpr int LOADS_PER_TILE = 3;    // copies per wave and tile: K value, K residual, V
+    __shared__ __attribute__((aligned(1024))) char tiles_lds[NKB * KBUF + NVB * T::VBYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -286,12 +306,15 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     const int N = p.Nk, Np = p.npad, ntile = Np / kFp8Tile;
     const int q0 = qt * BM;
     const size_t bhq = (size_t)b * p.Hq + h, bhk = (size_t)b * p.Hkv + g;
+    // packed buffers: value codes, residual codes (Q, K), then the tile scales
+    const size_t qplane = (size_t)p.B * p.Hq * Np * D, kplane = (size_t)p.B * p.Hkv * Np * D;
     const uint8_t* Q8 = (const uint8_t*)p.q + bhq * Np * D;
     const uint8_t* K8 = (const uint8_t*)p.k + bhk * Np * D;
+    const uint8_t* K8r = K8 + kplane;
     const uint8_t* V8 = (const uint8_t*)p.v + bhk * D * Np;
-    const float* qsc = (const float*)((const uint8_t*)p.q + (size_t)p.B * p.Hq * Np * D) + bhq * ntile;
-    const float* ksc = (const float*)((const uint8_t*)p.k + (size_t)p.B * p.Hkv * Np * D) + bhk * ntile;
-    const float* vsc = (const float*)((const uint8_t*)p.v + (size_t)p.B * p.Hkv * Np * D) + bhk * ntile;
+    const float* qsc = (const float*)((const uint8_t*)p.q + 2 * qplane) + bhq * ntile;
+    const float* ksc = (const float*)((const uint8_t*)p.k + 2 * kplane) + bhk * ntile;
+    const float* vsc = (const float*)((const uint8_t*)p.v + 2 * kplane) + bhk * ntile;
 
     const int wq0 = q0 + wave * 32;
     const bool wave_active = wq0 < N;
@@ -307,12 +330,16 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     const float sq = qsc[min(wq0, Np - 1) / kFp8Tile];
     const float c_q = sq * p.scale_log2;
 
-    // Q fragments: lane holds row l32, bytes 64 s + 32 hh .. + 31
-    i32x8 qf[2];
+    // Q fragments (value and residual codes): lane holds row l32, bytes
+    // 64 s + 32 hh .. + 31
+    i32x8 qf[2], qr2[2];
     {
         const uint8_t* qr = Q8 + (size_t)min(row, Np - 1) * D + 32 * hh;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) qf[s] = *(const i32x8*)(qr + 64 * s);
+        for (int s = 0; s < 2; ++s) {
+            qf[s] = *(const i32x8*)(qr + 64 * s);
+            qr2[s] = *(const i32x8*)(qr + qplane + 64 * s);
+        }
     }
     // Retire every compiler-visible global load before the loop: the tile
     // copies are inline asm the compiler does not count, so a pending load
@@ -329,15 +356,18 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     // Matrix operands written by vector code: set here, pinned in their
     // register files, followed by wait states before the first product.
 #pragma unroll
-    for (int s = 0; s < 2; ++s) pin_a(qf[s]);
+    for (int s = 0; s < 2; ++s) {
+        pin_a(qf[s]);
+        pin_a(qr2[s]);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) pin_a(o[t]);
     mfma_guard();
 
     ATTN_LDS char* lds = (ATTN_LDS char*)tiles_lds;
-    auto kbuf = [&](int i) __attribute__((always_inline)) { return lds + (i % NKB) * T::KBYTES; };
+    auto kbuf = [&](int i) __attribute__((always_inline)) { return lds + (i % NKB) * KBUF; };
     auto vbuf = [&](int i) __attribute__((always_inline)) {
-        return lds + NKB * T::KBYTES + (i % NVB) * T::VBYTES;
+        return lds + NKB * KBUF + (i % NVB) * T::VBYTES;
     };
     // Lane-constant fragment offsets. K: block kb, lane row pi(l32) (+16 kb),
     // 16-byte chunks 4 s + 2 hh + {0, 1}. V^T: row 32 t + l32 (the swizzle
@@ -366,6 +396,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     const unsigned cv_off = cv_row * Np + ((cv_pc ^ T::swz_v(cv_row)) << 4);
     auto tile_k = [&](int i) __attribute__((always_inline)) {
         dma16s(K8 + (size_t)i * BN * D, ck_off, lds_addr(kbuf(i)) + wave * 1024);
+        dma16s(K8r + (size_t)i * BN * D, ck_off, lds_addr(kbuf(i)) + T::KBYTES + wave * 1024);
     };
     auto tile_v = [&](int i) __attribute__((always_inline)) {
         dma16s(V8 + (size_t)i * BN, cv_off, lds_addr(vbuf(i)) + wave * 1024);
@@ -384,23 +415,36 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
                     ka[kb][st][hf] = sb + kofs[kb][st][hf];
                     pin(ka[kb][st][hf]);
                 }
-        i32x8 kf[4];
+        i32x8 kf[4], kr[4];   // value and residual fragments, i = (kb, st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {   // i = (kb, st)
+        for (int i = 0; i < 4; ++i) {
             const i32x4 lo = *(const ATTN_LDS i32x4*)at(ka[i >> 1][i & 1][0], 0);
             const i32x4 hi = *(const ATTN_LDS i32x4*)at(ka[i >> 1][i & 1][1], 0);
             kf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const i32x4 lo = *(const ATTN_LDS i32x4*)at(ka[i >> 1][i & 1][0], T::KBYTES);
+            const i32x4 hi = *(const ATTN_LDS i32x4*)at(ka[i >> 1][i & 1][1], T::KBYTES);
+            kr[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             if ((i & 1) == 0) mfma_fp8_va0(sacc[i >> 1], kf[i], qf[0]);
             else mfma_fp8_va(sacc[i >> 1], kf[i], qf[1]);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mfma_fp8_va(sacc[i >> 1], kf[i], qr2[i & 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mfma_fp8_va(sacc[i >> 1], kr[i], qf[i & 1]);
         mfma_guard();   // the scores may be read right after
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) pin(sacc[kb]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) keep(kf[i]);
+        for (int i = 0; i < 4; ++i) {
+            keep(kf[i]);
+            keep(kr[i]);
+        }
     };
 
     i32x8 pf = {};
@@ -511,7 +555,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     };
     auto barrier_and_copy = [&](int i, bool copy = true) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
+        if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
         else __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
