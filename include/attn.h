@@ -31,6 +31,19 @@
  *   kernel execution surface, as for any stream API, at the caller's next
  *   synchronisation.
  * - No call keeps mutable global state; calls are thread-safe.
+ *
+ * Debug aids (environment variables, read once per process):
+ * - ATTN_CHECK=1 checks preconditions on device data before launching:
+ *   doc_ids non-decreasing (attn_fwd with ATTN_MASK_DOC), cu_seqlens starting
+ *   at 0, non-decreasing and ending at total (attn_fwd_varlen), seq_lens
+ *   within max_blocks * block_size (attn_decode_paged); a violation returns
+ *   ATTN_ERR_INVALID_ARG and launches nothing. The data is copied to the host
+ *   and the stream synchronised: not for use under graph capture.
+ * - ATTN_LOG=1 prints each call's arguments to stderr and, for attn_fwd, the
+ *   grid and the forward's tile counts (blocks of 32 query rows by 64-key
+ *   tiles: empty = skipped, partial = element mask, full = no mask code) and
+ *   the skipped fraction. With ATTN_MASK_DOC it copies doc_ids to the host
+ *   and synchronises the stream, as ATTN_CHECK does.
  */
 #ifndef TILED_ATTN_H
 #define TILED_ATTN_H
@@ -203,6 +216,23 @@ size_t attn_block_mask_bytes(int B, int Nq, int Nk, int block_m, int block_n);
 int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window,
                           const int32_t* doc_ids, int block_m, int block_n,
                           void* out, void* stream);
+
+/*
+ * attn_fwd_tile_kinds -- the bf16 forward's own tile schedule, for inspection
+ * (same page and section: block sparsity). The forward gives each wave 32
+ * query rows and walks 64-key tiles; this writes, for every (batch row, block
+ * of 32 rows, key tile), the kind the forward kernel assigns through the same
+ * device functions: 0 = empty (skipped), 1 = partial (element mask), 2 = full
+ * (no mask code). It equals attn_block_mask_build's table at block_m = 32,
+ * block_n = 64, except that a ragged last key tile (Nk % 64 != 0) whose
+ * existing pairs are all allowed is partial here (the kernel masks the
+ * missing keys).
+ * out : device int8 [B][ceil(Nq/32)][ceil(Nk/64)], attn_fwd_tile_kinds_bytes
+ *       bytes (0 on bad sizes). Mask arguments and errors as attn_fwd.
+ */
+size_t attn_fwd_tile_kinds_bytes(int B, int Nq, int Nk);
+int attn_fwd_tile_kinds(int B, int Nq, int Nk, int mask_kind, int window,
+                        const int32_t* doc_ids, int8_t* out, void* stream);
 
 /*
  * attn_decode_paged -- one new token per sequence attending to its whole

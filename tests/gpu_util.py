@@ -1,4 +1,7 @@
 """Helpers of the GPU parity tests: upload, run, compare against the oracle."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -45,3 +48,26 @@ def assert_close(o_gpu, lse_gpu, O_ref, L_ref, max_abs=MAX_ABS, mean_abs=MEAN_AB
 def oracle(x, scale, mask, window=0, softcap=0.0, heads=None, rows=None):
     return A.attention(x["q"], x["k"], x["v"], scale, mask, window, x.get("doc_ids"), softcap,
                        x.get("slopes"), heads=heads, rows=rows)
+
+
+def oracle_whole_heads(x, w, heads, threads=None, chunk=1024):
+    """Every row of the given (b, h) heads, the oracle run on row chunks of
+    each head in parallel (rows are independent, so the result is the
+    untiled one). Returns (O [n, N, d], LSE [n, N])."""
+    from threadpoolctl import threadpool_limits
+    N = w.N
+    jobs = [(i, bh, np.arange(r0, min(r0 + chunk, N))) for i, bh in enumerate(heads) for r0 in range(0, N, chunk)]
+    O = np.empty((len(heads), N, w.d))
+    L = np.empty((len(heads), N))
+
+    def run(job):
+        i, bh, rows = job
+        o, l = A.attention(x["q"], x["k"], x["v"], w.scale, w.mask, w.window, x.get("doc_ids"), w.softcap,
+                           x.get("slopes"), heads=[bh], rows=rows, threads=1)
+        O[i, rows] = o[0]
+        L[i, rows] = l[0]
+
+    n = threads or min(16, len(os.sched_getaffinity(0)))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(n) as ex:
+        list(ex.map(run, jobs))
+    return O, L

@@ -160,3 +160,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_no_device_calls_return_hip_error(lib):
+    """With no GPU present, a call that passes validation reaches the HIP launch
+    and returns ATTN_ERR_HIP; nothing crashes. Skipped wherever a GPU is
+    visible: the pointers here are fake and must never reach a real launch."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+    F = FAKE
+    calls = {
+        "fwd": lambda: lib.attn_fwd(F, F, F, F, None, 1, 2, 2, 16, 16, 128, 0.1, 0, 0, None, 0.0, None, 1, None),
+        "fwd_fp8": lambda: lib.attn_fwd(F, F, F, F, None, 1, 2, 2, 16, 16, 128, 0.1, 0, 0, None, 0.0, None, 2,
+                                        None),
+        "varlen": lambda: lib.attn_fwd_varlen(F, F, F, F, None, F, 2, 16, 2, 2, 128, 0.1, 1, 0, 0.0, None, F, 1,
+                                              None),
+        "prepare": lambda: lib.attn_fp8_prepare(F, F, F, 1, 2, 2, 16, 128, None, F, F, F, None),
+        "block_mask": lambda: lib.attn_block_mask_build(1, 16, 16, 1, 0, None, 32, 64, F, None),
+        "tile_kinds": lambda: lib.attn_fwd_tile_kinds(1, 16, 16, 1, 0, None, F, None),
+        "decode": lambda: lib.attn_decode_paged(F, F, F, F, F, F, None, 1, 2, 2, 128, 16, 4, 0.1, 1, None, 1, None),
+        "bwd": lambda: lib.attn_bwd(F, F, F, F, F, F, F, F, F, F, 1, 2, 2, 16, 128, 0.1, 1, 1, None),
+    }
+    for name, call in calls.items():
+        assert call() == _lib.ERR_HIP, name

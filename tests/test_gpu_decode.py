@@ -23,6 +23,11 @@ CASES = [
     # equal and empty lengths: the sequences are launched longest first, ties by index
     (9, 4, 2, [50, 300, 50, 0, 300, 7, 1000, 50, 0], 4),
     (70, 4, 2, [(i * 37) % 50 * 7 for i in range(70)], 3),
+    # lengths equal to the table's capacity with an odd number of blocks: the last
+    # 32-key chunk's second page is past the row end and must not be read
+    (2, 4, 2, [48, 16], 2),
+    (1, 4, 1, [80], 1),
+    (3, 8, 2, [112, 112, 3], 4),
 ]
 
 

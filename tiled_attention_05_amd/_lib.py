@@ -23,8 +23,8 @@ MASK_NONE, MASK_CAUSAL, MASK_WINDOW, MASK_DOC = 0, 1, 2, 4
 FP8_TILE = 128
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_fp8_prepare_rope",
-           "attn_block_mask_bytes", "attn_block_mask_build", "attn_decode_workspace_floats", "attn_decode_paged",
-           "attn_bwd", "attn_status_string")
+           "attn_block_mask_bytes", "attn_block_mask_build", "attn_fwd_tile_kinds_bytes", "attn_fwd_tile_kinds",
+           "attn_decode_workspace_floats", "attn_decode_paged", "attn_bwd", "attn_status_string")
 
 _lib = None
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -67,6 +67,10 @@ def load():
         lib.attn_block_mask_bytes.argtypes = [_i, _i, _i, _i, _i]
         lib.attn_block_mask_build.restype = _i
         lib.attn_block_mask_build.argtypes = [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp]
+        lib.attn_fwd_tile_kinds_bytes.restype = _sz
+        lib.attn_fwd_tile_kinds_bytes.argtypes = [_i, _i, _i]
+        lib.attn_fwd_tile_kinds.restype = _i
+        lib.attn_fwd_tile_kinds.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [_i]
         _lib = lib
@@ -145,8 +149,18 @@ def attn_block_mask_build(B, Nq, Nk, mask_kind, window, doc_ids, block_m, block_
                                         _ptr(out), _stream(stream))
 
 
+def attn_fwd_tile_kinds_bytes(B, Nq, Nk) -> int:
+    return load().attn_fwd_tile_kinds_bytes(B, Nq, Nk)
+
+
+def attn_fwd_tile_kinds(B, Nq, Nk, mask_kind, window, doc_ids, out, stream=None) -> int:
+    return load().attn_fwd_tile_kinds(B, Nq, Nk, mask_kind, window, _ptr(doc_ids), _ptr(out), _stream(stream))
+
+
 # ------------------------------------------------------------------ helpers
-def _need(t, name, dtype=None, ndim=None):
+def _need(t, name, dtype=None, ndim=None, shape=None, numel=None):
+    """Check a device tensor argument; ``shape`` (exact) or ``numel`` (a lower
+    bound) guard the extent the kernels will read or write."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA/HIP tensor")
     if not t.is_contiguous():
@@ -155,6 +169,10 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} elements, got {t.numel()}")
 
 
 def fwd(q, k, v, scale=None, mask=MASK_NONE, window=0, doc_ids=None, softcap=0.0, alibi_slopes=None,
@@ -170,9 +188,13 @@ def fwd(q, k, v, scale=None, mask=MASK_NONE, window=0, doc_ids=None, softcap=0.0
     if v.shape != k.shape or k.shape[0] != B or k.shape[3] != d:
         raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
     if doc_ids is not None:
-        _need(doc_ids, "doc_ids", torch.int32, 2)
+        _need(doc_ids, "doc_ids", torch.int32, shape=(B, Nk))
     if alibi_slopes is not None:
-        _need(alibi_slopes, "alibi_slopes", torch.float32, 1)
+        _need(alibi_slopes, "alibi_slopes", torch.float32, 1, numel=Hq)
+    if out is not None:
+        _need(out, "out", q.dtype, shape=q.shape)
+    if with_lse and lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq, Nq))
     o = torch.empty_like(q) if out is None else out
     if with_lse and lse is None:
         lse = torch.empty(B, Hq, Nq, device=q.device, dtype=torch.float32)
@@ -198,9 +220,15 @@ def fwd_varlen(q, k, v, cu_seqlens, scale=None, mask=MASK_NONE, window=0, softca
     Hkv = k.shape[0]
     if v.shape != k.shape or k.shape[1] != total or k.shape[2] != d:
         raise ValueError("k and v must be [Hkv, total, d] matching q")
-    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, numel=2)
     if alibi_slopes is not None:
-        _need(alibi_slopes, "alibi_slopes", torch.float32, 1)
+        _need(alibi_slopes, "alibi_slopes", torch.float32, 1, numel=Hq)
+    if out is not None:
+        _need(out, "out", q.dtype, shape=q.shape)
+    if with_lse and lse is not None:
+        _need(lse, "lse", torch.float32, shape=(Hq, total))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.int32, numel=total)
     o = torch.empty_like(q) if out is None else out
     if with_lse and lse is None:
         lse = torch.empty(Hq, total, device=q.device, dtype=torch.float32)
@@ -215,11 +243,15 @@ def fwd_varlen(q, k, v, cu_seqlens, scale=None, mask=MASK_NONE, window=0, softca
 
 def bwd(q, k, v, o, dout, lse, scale=None, mask=MASK_NONE, workspace=None, stream=None):
     """(dQ, dK, dV) of the forward for output gradient dout (bf16 BHSD, d = 128)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _need(t, n, torch.bfloat16, 4)
-    _need(lse, "lse", torch.float32, 3)
+    _need(q, "q", torch.bfloat16, 4)
     B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    Hkv = k.shape[1] if isinstance(k, torch.Tensor) and k.dim() == 4 else 0
+    for t, n, shp in ((k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)), (o, "o", q.shape),
+                      (dout, "dout", q.shape)):
+        _need(t, n, torch.bfloat16, shape=shp)
+    _need(lse, "lse", torch.float32, shape=(B, Hq, N))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.float32, numel=B * Hq * N)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(B * Hq * N, device=q.device, dtype=torch.float32) if workspace is None else workspace
     sc = 1.0 / math.sqrt(d) if scale is None else scale
@@ -236,16 +268,24 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, num_spl
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     _need(v_cache, "v_cache", torch.bfloat16, 4)
-    _need(block_table, "block_table", torch.int32, 2)
-    _need(seq_lens, "seq_lens", torch.int32, 1)
     B, Hq, d = q.shape
+    _need(block_table, "block_table", torch.int32, 2)
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table must have {B} rows")
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,))
     _, Hkv, bs, _ = k_cache.shape
     if v_cache.shape != k_cache.shape or k_cache.shape[3] != d:
         raise ValueError("caches must be [num_blocks, Hkv, block_size, d] matching q")
+    if out is not None:
+        _need(out, "out", torch.bfloat16, shape=q.shape)
+    if with_lse and lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq))
     o = torch.empty_like(q) if out is None else out
     if with_lse and lse is None:
         lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
     n = attn_decode_workspace_floats(B, Hq, d, num_splits)
+    if workspace is not None and n > 0:
+        _need(workspace, "workspace", torch.float32, numel=n)
     ws = workspace
     if ws is None and n > 0:
         ws = torch.empty(n, device=q.device, dtype=torch.float32)
@@ -261,10 +301,13 @@ def fp8_prepare(q, k, v, signs, stream=None, rope_cos=None, rope_sin=None):
     """Rotate Q, K (random-sign Hadamard; none if signs is None) and quantise Q, K, V
     to packed e4m3 buffers. With rope_cos / rope_sin (float32 [N, d/2]) the
     rotary embedding of Q and K runs first, in the same kernel."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16, 4)
+    _need(q, "q", torch.bfloat16, 4)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1] if isinstance(k, torch.Tensor) and k.dim() == 4 else 0
+    _need(k, "k", torch.bfloat16, shape=(B, Hkv, N, d))
+    _need(v, "v", torch.bfloat16, shape=(B, Hkv, N, d))
     if signs is not None:
-        _need(signs, "signs", torch.int8, 1)
+        _need(signs, "signs", torch.int8, shape=(d,))
     if (rope_cos is None) != (rope_sin is None):
         raise ValueError("rope_cos and rope_sin go together")
     if rope_cos is not None:
@@ -272,8 +315,6 @@ def fp8_prepare(q, k, v, signs, stream=None, rope_cos=None, rope_sin=None):
         _need(rope_sin, "rope_sin", torch.float32, 2)
         if rope_cos.shape != (q.shape[2], q.shape[3] // 2) or rope_sin.shape != rope_cos.shape:
             raise ValueError("rope tables must be [N, d/2]")
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
     nq = attn_fp8_buffer_bytes(B, Hq, N, d)
     nk = attn_fp8_buffer_bytes(B, Hkv, N, d)
     q8 = torch.empty(nq, dtype=torch.uint8, device=q.device)
@@ -290,6 +331,12 @@ def fp8_prepare(q, k, v, signs, stream=None, rope_cos=None, rope_sin=None):
 
 def fwd_fp8(q8, k8, v8, B, Hq, Hkv, N, d, scale=None, with_lse=True, stream=None, out=None, lse=None):
     """O (bf16) and LSE of the fp8 forward on buffers written by fp8_prepare."""
+    for t, n, H in ((q8, "q8", Hq), (k8, "k8", Hkv), (v8, "v8", Hkv)):
+        _need(t, n, torch.uint8, 1, numel=attn_fp8_buffer_bytes(B, H, N, d))
+    if out is not None:
+        _need(out, "out", torch.bfloat16, shape=(B, Hq, N, d))
+    if with_lse and lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq, N))
     o = torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=q8.device) if out is None else out
     if with_lse and lse is None:
         lse = torch.empty(B, Hq, N, device=q8.device, dtype=torch.float32)
@@ -333,3 +380,20 @@ def block_mask(B, Nq, Nk, mask, window=0, doc_ids=None, block_m=128, block_n=64,
     counts = out[kb:kb + B * nq * 3 * 4].view(torch.int32).view(B, nq, 3)
     flags = out[kb + B * nq * 12:kb + B * nq * 12 + 4].view(torch.int32)
     return kinds, counts, flags
+
+
+def fwd_tile_kinds(B, Nq, Nk, mask, window=0, doc_ids=None, device="cuda", stream=None):
+    """int8 [B, ceil(Nq/32), ceil(Nk/64)]: the forward's own tile schedule
+    (0 empty, 1 partial, 2 full) for blocks of 32 query rows by 64-key tiles."""
+    n = attn_fwd_tile_kinds_bytes(B, Nq, Nk)
+    if n == 0:
+        raise AttnError(ERR_INVALID_ARG, "attn_fwd_tile_kinds_bytes")
+    if doc_ids is not None:
+        _need(doc_ids, "doc_ids", torch.int32, 2)
+        if tuple(doc_ids.shape) != (B, Nk):
+            raise ValueError(f"doc_ids must be [B, Nk] = [{B}, {Nk}]")
+    out = torch.empty(n, dtype=torch.int8, device=device)
+    st = attn_fwd_tile_kinds(B, Nq, Nk, mask, window, doc_ids, out, stream)
+    if st:
+        raise AttnError(st, "attn_fwd_tile_kinds")
+    return out.view(B, -(-Nq // 32), -(-Nk // 64))

@@ -3,10 +3,12 @@
 // sources are documented in include/attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "fwd_params.h"
@@ -20,6 +22,8 @@ hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, int B
                               void* k8, void* v8, hipStream_t st);
 hipError_t launch_block_mask(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int bm,
                              int bn, void* out, hipStream_t st);
+hipError_t launch_fwd_plan(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int8_t* kinds,
+                           hipStream_t st);
 hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* ids, hipStream_t st);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* table, const int32_t* lens,
                          void* o, float* lse, int B, int Hq, int Hkv, int max_blocks, float scale, int splits,
@@ -35,12 +39,72 @@ constexpr int kKnownMask = ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW | ATTN_MASK_DOC;
 constexpr int kFp8Tile = 128;
 constexpr long long kMaxElems = (1LL << 40);
 
+bool env_flag(const char* name) {
+    const char* e = std::getenv(name);
+    return e && e[0] && e[0] != '0';
+}
+
 bool log_enabled() {
-    static const bool on = [] {
-        const char* e = std::getenv("ATTN_LOG");
-        return e && e[0] && e[0] != '0';
-    }();
+    static const bool on = env_flag("ATTN_LOG");
     return on;
+}
+
+// ATTN_CHECK=1: debug-only synchronous checks of preconditions on device data
+// (document ids non-decreasing, sequence offsets monotone). They copy the data
+// to the host and synchronise the stream, so they must not be enabled under
+// graph capture.
+bool check_enabled() {
+    static const bool on = env_flag("ATTN_CHECK");
+    return on;
+}
+
+// Copies n int32 values from the device (stream-ordered, then waits).
+int fetch_i32(const int32_t* dev, size_t n, void* stream, std::vector<int32_t>& host) {
+    host.resize(n);
+    hipStream_t st = (hipStream_t)stream;
+    if (hipMemcpyAsync(host.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+// Tile counts of the bf16 / fp32 forward's schedule (blocks of 32 query rows,
+// one per wave, by 64-key tiles), the same rules as the kernels' range and
+// full-tile functions: a tile outside the rows' contiguous key range is
+// empty (skipped), one whose pairs are all allowed is full, the rest partial.
+struct PlanCounts {
+    long long empty = 0, partial = 0, full = 0;
+};
+PlanCounts plan_counts(int B, int Nq, int Nk, int mask, int W, const std::vector<int32_t>* docs) {
+    constexpr int RB = 32, BN = 64;
+    PlanCounts c;
+    const int off = Nk - Nq, n_kt = (Nk + BN - 1) / BN;
+    for (int b = 0; b < B; ++b) {
+        const int32_t* d = docs ? docs->data() + (size_t)b * Nk : nullptr;
+        for (int r0 = 0; r0 < Nq; r0 += RB) {
+            const int r1 = std::min(r0 + RB, Nq) - 1;
+            int lo = 0, hi = Nk, dq0 = 0, dq1 = 0;
+            if (mask & ATTN_MASK_CAUSAL) hi = std::min(hi, r1 + off + 1);
+            if (mask & ATTN_MASK_WINDOW) lo = std::max(lo, r0 + off - W + 1);
+            if (d) {
+                dq0 = d[r0];
+                dq1 = d[r1];
+                lo = std::max(lo, (int)(std::lower_bound(d, d + Nk, dq0) - d));
+                hi = std::min(hi, (int)(std::upper_bound(d, d + Nk, dq1) - d));
+            }
+            const int t0 = hi > lo ? lo / BN : 0, t1 = hi > lo ? (hi + BN - 1) / BN : 0;
+            c.empty += n_kt - (t1 - t0);
+            for (int kt = t0; kt < t1; ++kt) {
+                const int j0 = kt * BN, j1 = std::min(j0 + BN, Nk) - 1;
+                bool full = j0 + BN <= Nk;
+                if (mask & ATTN_MASK_CAUSAL) full &= j1 <= r0 + off;
+                if (mask & ATTN_MASK_WINDOW) full &= (r1 + off) - j0 < W;
+                if (d) full &= d[j0] == d[j1] && dq0 == dq1 && d[j0] == dq0;
+                (full ? c.full : c.partial) += 1;
+            }
+        }
+    }
+    return c;
 }
 
 // Mask / size checks shared by attn_fwd and the block-mask builder.
@@ -114,10 +178,30 @@ int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
     p.softcap = softcap;
     p.npad = (Nk + kFp8Tile - 1) / kFp8Tile * kFp8Tile;
     hipStream_t st = (hipStream_t)stream;
-    if (log_enabled())
+    std::vector<int32_t> docs;
+    if ((check_enabled() || log_enabled()) && (mask_kind & ATTN_MASK_DOC)) {
+        if (fetch_i32(doc_ids, (size_t)B * Nk, stream, docs)) return ATTN_ERR_HIP;
+        if (check_enabled())
+            for (int b = 0; b < B; ++b)
+                for (int j = 1; j < Nk; ++j)
+                    if (docs[(size_t)b * Nk + j] < docs[(size_t)b * Nk + j - 1]) {
+                        if (log_enabled())
+                            std::fprintf(stderr, "[attn] ATTN_CHECK: doc_ids[%d] decreases at %d\n", b, j);
+                        return ATTN_ERR_INVALID_ARG;
+                    }
+    }
+    if (log_enabled()) {
+        const int n_qt = (Nq + 255) / 256;
         std::fprintf(stderr, "[attn] fwd dtype=%d B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d mask=%d window=%d "
-                             "softcap=%g alibi=%d\n",
-                     dtype, B, Hq, Hkv, Nq, Nk, d, mask_kind, p.window, softcap, alibi_slopes != nullptr);
+                             "softcap=%g alibi=%d grid=%lld x 512 threads\n",
+                     dtype, B, Hq, Hkv, Nq, Nk, d, mask_kind, p.window, softcap, alibi_slopes != nullptr,
+                     (long long)n_qt * B * Hq);
+        const PlanCounts c = plan_counts(B, Nq, Nk, mask_kind, p.window, docs.empty() ? nullptr : &docs);
+        const long long tot = c.empty + c.partial + c.full;
+        std::fprintf(stderr, "[attn] tiles per query head (32 rows x 64 keys): empty=%lld partial=%lld full=%lld "
+                             "skip=%.4f\n",
+                     c.empty, c.partial, c.full, tot ? (double)c.empty / tot : 0.0);
+    }
     hipError_t e;
     if (dtype == ATTN_BF16) e = attn::launch_fwd_bf16(p, d, st);
     else if (dtype == ATTN_F32) e = attn::launch_fwd_f32(p, d, st);
@@ -150,6 +234,13 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
     if (const int r = fwd_check(q, k, v, o, 1, Hq, Hkv, total, total, d, scale, mask, window, workspace,
                                 softcap, alibi_slopes, dtype))
         return r;
+    if (check_enabled()) {   // offsets: 0 first, non-decreasing, total last
+        std::vector<int32_t> cu;
+        if (fetch_i32(cu_seqlens, (size_t)num_seqs + 1, stream, cu)) return ATTN_ERR_HIP;
+        bool ok = cu[0] == 0 && cu[num_seqs] == total;
+        for (int s2 = 1; s2 <= num_seqs; ++s2) ok &= cu[s2] >= cu[s2 - 1];
+        if (!ok) return ATTN_ERR_INVALID_ARG;
+    }
     if (log_enabled())
         std::fprintf(stderr, "[attn] fwd_varlen num_seqs=%d total=%d\n", num_seqs, total);
     if (const int r = hip_status(attn::launch_seq_ids(cu_seqlens, num_seqs, total, workspace, (hipStream_t)stream)))
@@ -207,6 +298,20 @@ int attn_block_mask_build(int B, int Nq, int Nk, int mask_kind, int window, cons
                                               block_n, out, (hipStream_t)stream));
 }
 
+size_t attn_fwd_tile_kinds_bytes(int B, int Nq, int Nk) {
+    if (B < 1 || Nq < 1 || Nk < 1) return 0;
+    return (size_t)B * ((Nq + 31) / 32) * ((Nk + 63) / 64);
+}
+
+int attn_fwd_tile_kinds(int B, int Nq, int Nk, int mask_kind, int window, const int32_t* doc_ids, int8_t* out,
+                        void* stream) {
+    if (!out || B < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_INVALID_ARG;
+    if (const int r = check_mask(Nq, Nk, mask_kind, window, doc_ids)) return r;
+    return hip_status(attn::launch_fwd_plan(B, Nq, Nk, mask_kind, (mask_kind & ATTN_MASK_WINDOW) ? window : 0,
+                                            (mask_kind & ATTN_MASK_DOC) ? doc_ids : nullptr, out,
+                                            (hipStream_t)stream));
+}
+
 size_t attn_decode_workspace_floats(int B, int Hq, int d, int num_splits) {
     if (B < 1 || Hq < 1 || d < 1 || num_splits < 1) return 0;
     if (num_splits == 1) return 0;
@@ -224,6 +329,12 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, c
     if (num_splits > 1 && !workspace) return ATTN_ERR_INVALID_ARG;
     if ((long long)B * Hq * num_splits > (1LL << 31) / 256) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_BF16 || d != 128 || block_size != 16 || Hq / Hkv > 32) return ATTN_ERR_UNSUPPORTED;
+    if (check_enabled()) {   // cached lengths within the table's capacity
+        std::vector<int32_t> lens;
+        if (fetch_i32(seq_lens, (size_t)B, stream, lens)) return ATTN_ERR_HIP;
+        for (int b = 0; b < B; ++b)
+            if (lens[b] < 0 || (long long)lens[b] > (long long)max_blocks * block_size) return ATTN_ERR_INVALID_ARG;
+    }
     if (log_enabled())
         std::fprintf(stderr, "[attn] decode_paged B=%d Hq=%d Hkv=%d max_blocks=%d splits=%d\n", B, Hq, Hkv,
                      max_blocks, num_splits);

@@ -152,21 +152,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     const int wq0 = q0 + wave * 32;
     const bool wave_active = wq0 < Nq;
     const int wq1 = min(wq0 + 32, Nq) - 1;
-    int w_lo = INT_MAX, w_hi = INT_MIN;
-    int dq0 = 0, dq1 = 0;
-    if (wave_active) {
-        w_lo = 0;
-        w_hi = Nk;
-        if (causal) w_hi = min(w_hi, wq1 + off + 1);
-        if (windowed) w_lo = max(w_lo, wq0 + off - W + 1);
-        if (DOC) {
-            dq0 = docrow[wq0];
-            dq1 = docrow[wq1];
-            w_lo = max(w_lo, wave_search<false>(docrow, Nk, dq0, lane));
-            w_hi = min(w_hi, wave_search<true>(docrow, Nk, dq1, lane));
-        }
-        if (w_hi <= w_lo) { w_lo = INT_MAX; w_hi = INT_MIN; }
-    }
+    KeyRange kr{INT_MAX, INT_MIN, 0, 0};
+    if (wave_active) kr = rows_key_range<DOC>(wq0, wq1, Nk, off, p.mask, W, docrow, lane);
+    const int w_lo = kr.lo, w_hi = kr.hi;
+    const int dq0 = kr.dq0;
     if (lane == 0) { range_lds[wave][0] = w_lo; range_lds[wave][1] = w_hi; }
     __syncthreads();
     int kv_lo = INT_MAX, kv_hi = INT_MIN;
@@ -321,15 +310,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 
     auto is_full = [&](int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) -> bool {
         const int j0 = kt * BN;
-        const int j1 = min(j0 + BN, Nk) - 1;
-        bool full = j0 + BN <= Nk;
-        if (causal) full &= j1 <= wq0 + off;
-        if (windowed) full &= (wq1 + off) - j0 < W;
+        int dj0 = 0, dj1 = 0;
         if (DOC) {
-            const int dj0 = dl[wave * BN], dj1 = dl[wave * BN + (j1 - j0)];
-            full &= dj0 == dj1 && dq0 == dq1 && dj0 == dq0;
+            dj0 = dl[wave * BN];
+            dj1 = dl[wave * BN + (min(j0 + BN, Nk) - 1 - j0)];
         }
-        return full;
+        return tile_full<DOC>(j0, Nk, wq0, wq1, off, p.mask, W, kr, dj0, dj1);
     };
 
     // Score modifiers and / or the element mask, in place: the scores become
@@ -591,6 +577,46 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         if (p.lse && hh == 0)
             p.lse[(size_t)(b * p.Hq + h) * Nq + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     }
+}
+
+// -----------------------------------------------------------------------------
+// The forward's own tile schedule, written out for inspection: for every
+// block of 32 query rows (one wave of the forward) and every 64-key tile,
+// 0 = empty (skipped), 1 = partial (element mask), 2 = full (no mask code),
+// from the same range and full-tile functions the forward kernel calls. One
+// wave per (batch row, row block).
+template <bool DOC>
+__global__ __launch_bounds__(64) void fwd_plan_kernel(int Nq, int Nk, int mask, int W, const int32_t* doc,
+                                                      int n_rb, int n_kt, int8_t* kinds) {
+    const int b = blockIdx.x / n_rb, rb = blockIdx.x % n_rb, lane = threadIdx.x;
+    const int r0 = rb * 32, r1 = min(r0 + 32, Nq) - 1, off = Nk - Nq;
+    const int32_t* docrow = DOC ? doc + (size_t)b * Nk : nullptr;
+    const KeyRange kr = rows_key_range<DOC>(r0, r1, Nk, off, mask, W, docrow, lane);
+    const int t0 = kr.hi > kr.lo ? kr.lo / BN : 0, t1 = kr.hi > kr.lo ? (kr.hi + BN - 1) / BN : 0;
+    int8_t* out = kinds + ((size_t)b * n_rb + rb) * n_kt;
+    for (int kt = lane; kt < n_kt; kt += 64) {
+        int kind = 0;
+        if (kt >= t0 && kt < t1) {
+            const int j0 = kt * BN, j1 = min(j0 + BN, Nk) - 1;
+            kind = tile_full<DOC>(j0, Nk, r0, r1, off, mask, W, kr, DOC ? docrow[j0] : 0, DOC ? docrow[j1] : 0)
+                       ? 2 : 1;
+        }
+        out[kt] = (int8_t)kind;
+    }
+}
+
+hipError_t launch_fwd_plan(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int8_t* kinds,
+                           hipStream_t st) {
+    const int n_rb = (Nq + 31) / 32, n_kt = (Nk + BN - 1) / BN;
+    const long long grid = (long long)B * n_rb;
+    if (grid > INT_MAX) return hipErrorInvalidValue;
+    if (mask & kMaskDoc)
+        hipLaunchKernelGGL(fwd_plan_kernel<true>, dim3((unsigned)grid), dim3(64), 0, st, Nq, Nk, mask, window,
+                           doc, n_rb, n_kt, kinds);
+    else
+        hipLaunchKernelGGL(fwd_plan_kernel<false>, dim3((unsigned)grid), dim3(64), 0, st, Nq, Nk, mask, window,
+                           doc, n_rb, n_kt, kinds);
+    return hipGetLastError();
 }
 
 // -----------------------------------------------------------------------------

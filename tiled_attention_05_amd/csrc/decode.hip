@@ -77,7 +77,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     // (clamped: a sequence index outside 0 .. B - 1 can never be addressed)
     const int b = p.order ? min(max(p.order[slot], 0), p.B - 1) : slot;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int L = p.lens[b];
+    // cached length, clamped to what the table row can address (a longer
+    // length would walk past the row into the next sequence's entries)
+    const int L = min(max(p.lens[b], 0), p.max_blocks * kPage);
     const int nch = (L + kCh - 1) / kCh;
     const int cps = (nch + p.splits - 1) / p.splits;
     const int c0 = min(split * cps, nch), c1 = min(c0 + cps, nch);

@@ -1,6 +1,8 @@
 // Pieces shared by the forward kernels: key-tile geometry and LDS swizzles,
 // the wave-parallel search over document ids, and the K/V tile copy.
 #pragma once
+#include <climits>
+
 #include "common.h"
 #include "fwd_params.h"
 
@@ -45,6 +47,52 @@ __device__ int wave_search(const int32_t* a, int n, int x, int lane) {
     if (j < hi) hit = STRICT ? (a[j] > x) : (a[j] >= x);
     const uint64_t bal = __ballot(hit);
     return bal ? min(hi, lo + __builtin_ctzll(bal)) : hi;
+}
+
+// Keys a block of query rows [r0, r1] (inclusive, r1 < Nq) may attend to: one
+// contiguous range [lo, hi), the union of the rows' allowed keys (causal: up
+// to r1 + off; window: from r0 + off - W + 1; documents: from the first key of
+// the first row's document to the last key of the last row's document, ids
+// being non-decreasing). Every key of the range is allowed for some row of
+// the block, so a key tile that meets the range is not empty. An empty range
+// comes back as lo = INT_MAX, hi = INT_MIN. dq0 / dq1: the document ids of
+// rows r0 and r1 (0 without documents). Called by a whole wave (the document
+// search is wave-parallel).
+struct KeyRange {
+    int lo, hi, dq0, dq1;
+};
+template <bool DOC>
+__device__ __forceinline__ KeyRange rows_key_range(int r0, int r1, int Nk, int off, int mask, int W,
+                                                   const int32_t* docrow, int lane) {
+    KeyRange k{0, Nk, 0, 0};
+    if (mask & kMaskCausal) k.hi = min(k.hi, r1 + off + 1);
+    if (mask & kMaskWindow) k.lo = max(k.lo, r0 + off - W + 1);
+    if (DOC) {
+        k.dq0 = docrow[r0];
+        k.dq1 = docrow[r1];
+        k.lo = max(k.lo, wave_search<false>(docrow, Nk, k.dq0, lane));
+        k.hi = min(k.hi, wave_search<true>(docrow, Nk, k.dq1, lane));
+    }
+    if (k.hi <= k.lo) {
+        k.lo = INT_MAX;
+        k.hi = INT_MIN;
+    }
+    return k;
+}
+
+// Whether every pair of rows [r0, r1] x keys of the tile starting at j0 is
+// allowed, so the tile needs no element mask ("full"); a ragged last tile
+// (fewer than BN keys) is never full, its missing keys being masked. dj0 / dj1:
+// document ids of the tile's first and last key.
+template <bool DOC>
+__device__ __forceinline__ bool tile_full(int j0, int Nk, int r0, int r1, int off, int mask, int W,
+                                          const KeyRange& k, int dj0, int dj1) {
+    const int j1 = min(j0 + BN, Nk) - 1;
+    bool full = j0 + BN <= Nk;
+    if (mask & kMaskCausal) full &= j1 <= r0 + off;
+    if (mask & kMaskWindow) full &= (r1 + off) - j0 < W;
+    if (DOC) full &= dj0 == dj1 && k.dq0 == k.dq1 && dj0 == k.dq0;
+    return full;
 }
 
 // Copy of one BN-row tile of K (or V) into LDS with its swizzle: LDS slot s
