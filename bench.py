@@ -89,7 +89,8 @@ def mask_name(m):
 
 
 def run_cpu_baseline(w, x, budget_s=15.0):
-    """Oracle on whole heads of the same inputs until ~budget_s of wall time."""
+    """Oracle on whole heads of the same inputs until ~budget_s of wall time.
+    Returns (summary, {(b, h): (O, LSE)} of the heads it computed)."""
     from oracle import attention as A
     threads = max(1, min(HOST_CORES, len(os.sched_getaffinity(0))))
     heads_all = [(b, h) for b in range(w.B) for h in range(w.Hq)]
@@ -99,13 +100,16 @@ def run_cpu_baseline(w, x, budget_s=15.0):
     per_head = flops.attention_flops(1, 1, w.N, w.N, w.d, w.mask, w.window,
                                      None if docs is None else docs[:1])
     i = 0
+    results = {}
     while time.perf_counter() - t0 < budget_s and i < len(order):
         batch = [hb for hb in order[i:i + threads] if hb not in done]
         i += threads
         if not batch:
             continue
-        A.attention(x["q"], x["k"], x["v"], w.scale, w.mask, w.window, docs, w.softcap, x["slopes"],
-                    heads=batch, threads=threads)
+        O, L = A.attention(x["q"], x["k"], x["v"], w.scale, w.mask, w.window, docs, w.softcap, x["slopes"],
+                           heads=batch, threads=threads)
+        for j, hb in enumerate(batch):
+            results[hb] = (O[j], L[j])
         for b, h in batch:
             row = None if docs is None else docs[b:b + 1]
             fl += flops.attention_flops(1, 1, w.N, w.N, w.d, w.mask, w.window, row)
@@ -116,7 +120,35 @@ def run_cpu_baseline(w, x, budget_s=15.0):
                       f"float64 numpy, {dt:.1f} s wall",
             "seconds": round(dt, 2), "flops_per_head": per_head,
             "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
-                     "pool_threads": threads, "blas_threads_per_job": 1}}
+                     "pool_threads": threads, "blas_threads_per_job": 1}}, results
+
+
+def parity_of_timed_output(w, o, lse, results):
+    """The timed launches' output (the last one's O and LSE) against the oracle
+    heads the CPU baseline computed: max-abs / mean-abs over O and max LSE
+    error (bf16 / fp32 bars), or relative RMS (fp8 bar)."""
+    import numpy as np
+    heads = sorted(results)
+    if not heads:
+        return None
+    og = torch.stack([o[b, h] for b, h in heads]).float().cpu().double().numpy()
+    lg = torch.stack([lse[b, h] for b, h in heads]).cpu().double().numpy()
+    O = np.stack([results[hb][0] for hb in heads])
+    L = np.stack([results[hb][1] for hb in heads])
+    fin = np.isfinite(L)
+    out = {"heads": len(heads), "of": w.B * w.Hq, "rows": "all",
+           "lse_max": float(np.abs(lg[fin] - L[fin]).max()) if fin.any() else 0.0}
+    if w.dtype == "fp8":
+        per = np.sqrt(((og - O) ** 2).sum(axis=(1, 2)) / (O ** 2).sum(axis=(1, 2)))
+        out.update({"relrms": float(np.linalg.norm(og - O) / np.linalg.norm(O)),
+                    "relrms_head_max": float(per.max()), "bar": {"relrms": 5e-2}})
+        out["ok"] = out["relrms"] <= 5e-2 and out["relrms_head_max"] <= 5e-2
+    else:
+        err = np.abs(og - O)
+        out.update({"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                    "bar": {"max_abs": 2e-2, "mean_abs": 2e-3, "lse": 1e-3}})
+        out["ok"] = out["max_abs"] <= 2e-2 and out["mean_abs"] <= 2e-3 and out["lse_max"] <= 1e-3
+    return out
 
 
 def bench_decode(w, args):
@@ -349,7 +381,10 @@ def main():
     elif extra:
         out["config"].update(extra)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = run_cpu_baseline(w, x, args.cpu_seconds)
+        out["cpu_baseline"], results = run_cpu_baseline(w, x, args.cpu_seconds)
+        if w.extra.get("varlen"):
+            results = {}   # the packed layout is checked by the varlen tests, not here
+        out["parity"] = parity_of_timed_output(w, o, lse, results)
     print(json.dumps(out), flush=True)
 
 
