@@ -272,6 +272,24 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int num_splits, float* workspace, int dtype, void* stream);
 
 /*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without `workspace`,
+ * the same kernels and results. The split outputs, LSEs and launch order live
+ * in a fixed device array of the library, 16 MiB (4 * 2^20 floats) per GPU,
+ * held until the process ends. attn_decode_workspace_floats(B, Hq, d,
+ * num_splits) must not exceed 4 * 2^20, else ATTN_ERR_INVALID_ARG (nothing
+ * launched). Calls that overlap in time on one GPU (different streams) share
+ * the array and race: serialise them. The call allocates nothing and makes
+ * no allocating runtime call; the array's device address is looked up once
+ * per device. Errors otherwise as attn_decode_paged.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                              int B, int Hq, int Hkv, int d, int block_size, int max_blocks, float scale,
+                              int num_splits, int dtype, void* stream);
+
+/*
  * attn_bwd -- gradients of attn_fwd (no modifiers) for an output gradient dO.
  * With P_ij = exp(scale q_i . k_j - LSE_i) recomputed from the forward's LSE
  * and D_i = sum_c dO_ic O_ic:

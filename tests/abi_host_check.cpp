@@ -37,6 +37,12 @@ hipError_t launch_decode(const void*, const void*, const void*, const int32_t*, 
     ++launches;
     return hipSuccess;
 }
+hipError_t launch_decode_noalloc(const void*, const void*, const void*, const int32_t*, const int32_t*, void*,
+                                 float*, int, int, int, int, float, int, hipStream_t) {
+    ++launches;
+    return hipSuccess;
+}
+size_t decode_scratch_floats() { return size_t(4) << 20; }
 hipError_t launch_bwd(const void*, const void*, const void*, const void*, const void*, const float*, void*, void*,
                       void*, float*, int, int, int, int, float, int, hipStream_t) {
     ++launches;
@@ -129,6 +135,16 @@ int main() {
            ATTN_ERR_INVALID_ARG, 0);
     EXPECT(attn_decode_paged(P, P, P, D, D, P, nullptr, 4, 8, 2, 128, 8, 10, 0.1f, 1, nullptr, ATTN_BF16, nullptr),
            ATTN_ERR_UNSUPPORTED, 0);
+    EXPECT(attn_decode_paged_noalloc(P, P, P, D, D, P, nullptr, 64, 32, 8, 128, 16, 512, 0.1f, 8, ATTN_BF16,
+                                     nullptr),
+           ATTN_OK, 1);
+    // 256 x 64 heads x 16 splits x 129 floats: beyond the fixed scratch
+    EXPECT(attn_decode_paged_noalloc(P, P, P, D, D, P, nullptr, 256, 64, 8, 128, 16, 512, 0.1f, 16, ATTN_BF16,
+                                     nullptr),
+           ATTN_ERR_INVALID_ARG, 0);
+    EXPECT(attn_decode_paged_noalloc(nullptr, P, P, D, D, P, nullptr, 4, 8, 2, 128, 16, 10, 0.1f, 4, ATTN_BF16,
+                                     nullptr),
+           ATTN_ERR_INVALID_ARG, 0);
     EXPECT(attn_bwd(P, P, P, P, P, (const float*)P, P, P, P, (float*)P, 1, 2, 2, 16, 128, 0.1f, ATTN_MASK_CAUSAL,
                     ATTN_BF16, nullptr),
            ATTN_OK, 1);

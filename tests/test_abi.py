@@ -180,6 +180,8 @@ def test_no_device_calls_return_hip_error(lib):
         "block_mask": lambda: lib.attn_block_mask_build(1, 16, 16, 1, 0, None, 32, 64, F, None),
         "tile_kinds": lambda: lib.attn_fwd_tile_kinds(1, 16, 16, 1, 0, None, F, None),
         "decode": lambda: lib.attn_decode_paged(F, F, F, F, F, F, None, 1, 2, 2, 128, 16, 4, 0.1, 1, None, 1, None),
+        "decode_noalloc": lambda: lib.attn_decode_paged_noalloc(F, F, F, F, F, F, None, 1, 2, 2, 128, 16, 4, 0.1, 2,
+                                                                1, None),
         "bwd": lambda: lib.attn_bwd(F, F, F, F, F, F, F, F, F, F, 1, 2, 2, 16, 128, 0.1, 1, 1, None),
     }
     for name, call in calls.items():

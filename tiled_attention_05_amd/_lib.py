@@ -24,7 +24,8 @@ FP8_TILE = 128
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fp8_buffer_bytes", "attn_fp8_prepare", "attn_fp8_prepare_rope",
            "attn_block_mask_bytes", "attn_block_mask_build", "attn_fwd_tile_kinds_bytes", "attn_fwd_tile_kinds",
-           "attn_decode_workspace_floats", "attn_decode_paged", "attn_bwd", "attn_status_string")
+           "attn_decode_workspace_floats", "attn_decode_paged", "attn_decode_paged_noalloc", "attn_bwd",
+           "attn_status_string")
 
 _lib = None
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -61,6 +62,9 @@ def load():
         lib.attn_decode_paged.restype = _i
         lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
                                           _i, _vp]
+        lib.attn_decode_paged_noalloc.restype = _i
+        lib.attn_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                                  _i, _i, _vp]
         lib.attn_bwd.restype = _i
         lib.attn_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp]
         lib.attn_block_mask_bytes.restype = _sz
@@ -132,6 +136,13 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq,
     return load().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                     _ptr(o), _ptr(lse), B, Hq, Hkv, d, block_size, max_blocks, scale, num_splits,
                                     _ptr(workspace), dtype, _stream(stream))
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv, d, block_size,
+                              max_blocks, scale, num_splits, dtype, stream=None) -> int:
+    return load().attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                            _ptr(seq_lens), _ptr(o), _ptr(lse), B, Hq, Hkv, d, block_size,
+                                            max_blocks, scale, num_splits, dtype, _stream(stream))
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, mask_kind, dtype,

@@ -28,6 +28,10 @@ hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* i
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* table, const int32_t* lens,
                          void* o, float* lse, int B, int Hq, int Hkv, int max_blocks, float scale, int splits,
                          float* workspace, hipStream_t st);
+hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, const int32_t* table,
+                                 const int32_t* lens, void* o, float* lse, int B, int Hq, int Hkv, int max_blocks,
+                                 float scale, int splits, hipStream_t st);
+size_t decode_scratch_floats();
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, float scale,
                       int causal, hipStream_t st);
@@ -319,14 +323,19 @@ size_t attn_decode_workspace_floats(int B, int Hq, int d, int num_splits) {
     return (size_t)B * Hq * num_splits * (d + 1) + (size_t)B;
 }
 
-int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                      const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d, int block_size,
-                      int max_blocks, float scale, int num_splits, float* workspace, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of attn_decode_paged except the workspace, with no HIP call
+// other than ATTN_CHECK's length copy.
+int decode_check(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                 const int32_t* seq_lens, const void* o, int B, int Hq, int Hkv, int d, int block_size,
+                 int max_blocks, float scale, int num_splits, int dtype, void* stream) {
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || block_size < 1 || max_blocks < 1) return ATTN_ERR_INVALID_ARG;
     if (Hq % Hkv || !std::isfinite(scale) || num_splits < 1 || num_splits > 256) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
-    if (num_splits > 1 && !workspace) return ATTN_ERR_INVALID_ARG;
     if ((long long)B * Hq * num_splits > (1LL << 31) / 256) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_BF16 || d != 128 || block_size != 16 || Hq / Hkv > 32) return ATTN_ERR_UNSUPPORTED;
     if (check_enabled()) {   // cached lengths within the table's capacity
@@ -335,11 +344,45 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, c
         for (int b = 0; b < B; ++b)
             if (lens[b] < 0 || (long long)lens[b] > (long long)max_blocks * block_size) return ATTN_ERR_INVALID_ARG;
     }
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d, int block_size,
+                      int max_blocks, float scale, int num_splits, float* workspace, int dtype, void* stream) {
+    if (const int r = decode_check(q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv, d, block_size,
+                                   max_blocks, scale, num_splits, dtype, stream))
+        return r;
+    if (num_splits > 1 && !workspace) return ATTN_ERR_INVALID_ARG;
     if (log_enabled())
         std::fprintf(stderr, "[attn] decode_paged B=%d Hq=%d Hkv=%d max_blocks=%d splits=%d\n", B, Hq, Hkv,
                      max_blocks, num_splits);
     return hip_status(attn::launch_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv,
                                           max_blocks, scale, num_splits, workspace, (hipStream_t)stream));
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d,
+                              int block_size, int max_blocks, float scale, int num_splits, int dtype, void* stream) {
+    if (const int r = decode_check(q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv, d, block_size,
+                                   max_blocks, scale, num_splits, dtype, stream))
+        return r;
+    const size_t need = attn_decode_workspace_floats(B, Hq, d, num_splits);
+    if (need > attn::decode_scratch_floats()) {
+        if (log_enabled())
+            std::fprintf(stderr, "[attn] decode_paged_noalloc: %zu workspace floats needed, the fixed scratch "
+                                 "holds %zu\n", need, attn::decode_scratch_floats());
+        return ATTN_ERR_INVALID_ARG;
+    }
+    if (log_enabled())
+        std::fprintf(stderr, "[attn] decode_paged_noalloc B=%d Hq=%d Hkv=%d max_blocks=%d splits=%d\n", B, Hq, Hkv,
+                     max_blocks, num_splits);
+    return hip_status(attn::launch_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv,
+                                                  max_blocks, scale, num_splits, (hipStream_t)stream));
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

@@ -20,6 +20,8 @@
 // the kernel is bound by HBM, not by the padded products.
 #include <climits>
 
+#include <mutex>
+
 #include "fwd_common.h"
 
 namespace attn {
@@ -284,6 +286,53 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
     if (e != hipSuccess || splits == 1) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * Hq)), dim3(128), 0, st, p);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Workspace without allocation: a fixed device array holding the split
+// outputs, LSEs and launch order of attn_decode_paged_noalloc. Every GPU the
+// library runs on keeps its own copy until the process ends. In host code the
+// array's name is not a device address: the address is looked up once per
+// device (with that device current) and only that pointer is handed to the
+// kernels. Calls on one GPU share the array, so calls that overlap in time on
+// one GPU (concurrent streams) race; every entry a call reads is written
+// earlier in the same call, so nothing needs clearing between calls.
+constexpr size_t kDecodeScratchFloats = size_t(4) << 20;   // 16 MiB
+static __device__ __align__(256) float scratch[kDecodeScratchFloats];
+
+size_t decode_scratch_floats() { return kDecodeScratchFloats; }
+
+static float* scratch_ptr_for_current_device(hipError_t& err) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float* ptrs[kMaxDevices] = {};
+    int dev = 0;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return nullptr;
+        ptrs[dev] = (float*)ptr;
+    }
+    return ptrs[dev];
+}
+
+hipError_t launch_decode_noalloc(const void* q, const void* kc, const void* vc, const int32_t* table,
+                                 const int32_t* lens, void* o, float* lse, int B, int Hq, int Hkv, int max_blocks,
+                                 float scale, int splits, hipStream_t st) {
+    float* ws = nullptr;
+    if (splits > 1) {
+        hipError_t e;
+        ws = scratch_ptr_for_current_device(e);
+        if (!ws) return e;
+    }
+    return launch_decode(q, kc, vc, table, lens, o, lse, B, Hq, Hkv, max_blocks, scale, splits, ws, st);
 }
 
 }  // namespace attn
