@@ -260,3 +260,42 @@ def test_binding_rejects_bad_shapes():
     o = torch.empty(2, 4, 128, 128, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         _lib.fwd_fp8(torch.empty(100, dtype=torch.uint8, device="cuda"), q, q, 2, 4, 2, 128, 128, out=o)
+
+
+_PERSIST_CHILD = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from tests.test_gpu_fwd import persistent_cases
+outs = persistent_cases()
+torch.save([(o.cpu(), l.cpu()) for o, l in outs], sys.argv[2])
+"""
+
+
+def persistent_cases():
+    """Outputs of a few launches (causal, GQA + window, documents + mods, varlen)."""
+    outs = []
+    for w, docs in ((I.WORKLOADS[2].shrink(B=2, Hq=8, Hkv=8, N=1000), None),
+                    (I.WORKLOADS[3].shrink(B=1, Hq=16, Hkv=4, N=1500, window=300), None),
+                    (I.WORKLOADS[4].shrink(B=1, Hq=4, Hkv=4, N=2500), (64, 1024))):
+        outs.append(run_fwd(_case(w, doc_range=docs), w.mask, w.window, w.softcap))
+    return outs
+
+
+def test_persistent_launch_bitwise_equal():
+    """ATTN_PERSISTENT=1 (a resident-sized grid walking the items in the same
+    order) gives exactly the outputs of the one-workgroup-per-item launch."""
+    import os
+    import subprocess
+    import sys
+    import tempfile
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with tempfile.TemporaryDirectory() as td:
+        path = os.path.join(td, "persistent.pt")
+        env = dict(os.environ, ATTN_PERSISTENT="1")
+        r = subprocess.run([sys.executable, "-c", _PERSIST_CHILD, root, path], capture_output=True, text=True,
+                           env=env, timeout=300)
+        assert r.returncode == 0, r.stderr[-3000:]
+        got = torch.load(path, weights_only=True)
+    want = persistent_cases()
+    for (o, l), (o2, l2) in zip(want, got):
+        assert torch.equal(o.cpu(), o2) and torch.equal(l.cpu(), l2)

@@ -51,6 +51,7 @@
 // for causal / window, from the tile's first / last document id for packed
 // documents.
 #include <climits>
+#include <cstdlib>
 #include <type_traits>
 
 #include "fwd_common.h"
@@ -81,8 +82,20 @@ namespace attn {
 constexpr float kLazyTau = 8.f;     // log2 units: rescale O only when the max grows by > 2^8
 constexpr float kNoMax = -1e30f;    // initial reference: finite, below any score
 
+// LDS of one workgroup of the bf16 forward.
+template <int D, bool DOC>
+struct Bf16Lds {
+    static constexpr int NW = 8, PF = ATTN_PREFETCH, NKB = PF + 1, NVB = PF + 2;
+    __attribute__((aligned(1024))) char tiles[(NKB + NVB) * Tile<D>::BYTES];
+    __attribute__((aligned(16))) int docs[DOC ? NVB * NW * BN : 4];
+    int range[NW][2];
+};
+
+// One work item (query tile qt of one (batch, head)) of the bf16 forward,
+// run by the whole workgroup; wid is the item's index in the launch order.
 template <int D, bool SOFTCAP, bool ALIBI, bool DOC>
-__global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
+__device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p, int wid,
+                                                             Bf16Lds<D, DOC>& sm) {
     using T = Tile<D>;
     constexpr int NW = 8;        // waves: 4 in group A, 4 in group B
     constexpr int BM = NW * 32;
@@ -106,9 +119,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     using Copy = TileCopy<D, A_ONLY ? NW / 2 : NW>;
     constexpr int LOADS_PER_TILE = 2 * Copy::ROUNDS + (DOC ? 1 : 0);   // per copying wave
 
-    __shared__ __attribute__((aligned(1024))) char tiles_lds[(NKB + NVB) * T::BYTES];
-    __shared__ __attribute__((aligned(16))) int docs_lds[DOC ? NVB * NW * BN : 4];
-    __shared__ int range_lds[NW][2];
+    char* tiles_lds = sm.tiles;
+    int* docs_lds = sm.docs;
+    auto& range_lds = sm.range;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -116,7 +129,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     const int l32 = lane & 31, hh = lane >> 5;
 
     // ---- work item: heavy (late) query tiles first for causal balance
-    const int wid = blockIdx.x;
     int qt = p.n_qt - 1 - wid / p.n_bh;
     // (batch, head) slot j. Round-robin dispatch puts workgroup w on XCD
     // w % 8. With xgrp > 0 each XCD takes its heads xgrp at a time, all
@@ -579,6 +591,27 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     }
 }
 
+// One workgroup per work item (the grid is every item of the launch).
+template <int D, bool SOFTCAP, bool ALIBI, bool DOC>
+__global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
+    __shared__ Bf16Lds<D, DOC> sm;
+    fwd_bf16_item<D, SOFTCAP, ALIBI, DOC>(p, blockIdx.x, sm);
+}
+
+// Persistent form: a grid of as many workgroups as are resident at once, each
+// walking the items w, w + G, w + 2G, ... of the same heavy-first, XCD-grouped
+// order (a static schedule, no atomics); a barrier separates consecutive items
+// so no wave refills LDS buffers another wave still reads.
+template <int D, bool SOFTCAP, bool ALIBI, bool DOC>
+__global__ __launch_bounds__(512) void fwd_bf16_persistent_kernel(FwdParams p) {
+    __shared__ Bf16Lds<D, DOC> sm;
+    const int n_items = p.n_qt * p.n_bh;
+    for (int wid = blockIdx.x; wid < n_items; wid += gridDim.x) {
+        fwd_bf16_item<D, SOFTCAP, ALIBI, DOC>(p, wid, sm);
+        __syncthreads();
+    }
+}
+
 // -----------------------------------------------------------------------------
 // The forward's own tile schedule, written out for inspection: for every
 // block of 32 query rows (one wave of the forward) and every 64-key tile,
@@ -620,6 +653,25 @@ hipError_t launch_fwd_plan(int B, int Nq, int Nk, int mask, int window, const in
 }
 
 // -----------------------------------------------------------------------------
+// ATTN_PERSISTENT=1 (read once) selects the persistent form of the bf16
+// forward, for comparing the two launch forms; results are identical.
+static bool persistent_launch() {
+    static const bool on = [] {
+        const char* e = std::getenv("ATTN_PERSISTENT");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+// Compute units of the current device (one resident workgroup each).
+static int resident_workgroups() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    return n;
+}
+
 template <int D, bool SC, bool AL, bool DC>
 static hipError_t launch_bf16_inst(const FwdParams& p0, hipStream_t st) {
     FwdParams p = p0;
@@ -638,7 +690,14 @@ static hipError_t launch_bf16_inst(const FwdParams& p0, hipStream_t st) {
         while (g > 1 && per_xcd % g) --g;
         p.xgrp = g >= 2 ? g : 0;
     }
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, SC, AL, DC>), dim3(p.n_qt * p.n_bh), dim3(512), 0, st, p);
+    const int n_items = p.n_qt * p.n_bh;
+    if (persistent_launch()) {
+        // one workgroup per CU is resident (the LDS holds one workgroup's buffers)
+        const int grid = n_items < resident_workgroups() ? n_items : resident_workgroups();
+        hipLaunchKernelGGL((fwd_bf16_persistent_kernel<D, SC, AL, DC>), dim3(grid), dim3(512), 0, st, p);
+    } else {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, SC, AL, DC>), dim3(n_items), dim3(512), 0, st, p);
+    }
     return hipGetLastError();
 }
 
