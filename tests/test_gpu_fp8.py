@@ -289,3 +289,26 @@ def test_fp8_forward_after_rope_prepare():
     print(f"[fp8-rope] relRMS vs emulation {r:.3e}, lse {np.abs(lg - Le).max():.3e}", flush=True)
     assert r <= 1e-2
     assert np.abs(lg - Le).max() <= 1e-3
+
+
+@pytest.mark.parametrize("factor", [20.0, 1000.0])
+def test_fp8_v_outlier_token(factor):
+    """One V token scaled by a large factor: its tile's V scale is the head's
+    largest, so every other tile's probabilities are stored shrunk by
+    s_v / s_vmax. Against the exact float64 attention the relative RMS stays
+    within the fp8 bar, whole output and per head."""
+    w = I.WORKLOADS[5].shrink(B=1, Hq=2, Hkv=2, N=2048)
+    print(f"[case] fp8 V outlier token x{factor}", flush=True)
+    x = I.inputs(w)
+    v = x["v"].float()
+    v[:, :, 777, :] *= factor
+    x["v"] = v.to(torch.bfloat16)
+    q8, k8, v8 = _lib.fp8_prepare(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), x["signs"].cuda())
+    o = _lib.fwd_fp8(q8, k8, v8, w.B, w.Hq, w.Hkv, w.N, 128, scale=w.scale, with_lse=False)
+    torch.cuda.synchronize()
+    O, _ = A.attention(x["q"], x["k"], x["v"], w.scale)
+    og = o.float().cpu().double().numpy()
+    tot = _relrms(og, O)
+    per = max(_relrms(og[0, h], O[0, h]) for h in range(w.Hq))
+    print(f"[fp8-v-outlier] x{factor}: relRMS {tot:.4f}, per head max {per:.4f}", flush=True)
+    assert tot <= FP8_RELRMS and per <= FP8_RELRMS

@@ -62,6 +62,11 @@ namespace attn {
 constexpr float kTanhPolyU = 0.5f;
 constexpr float kTanhP0 = 0.999999463558197f, kTanhP1 = -0.33326318860054016f;
 constexpr float kTanhP2 = 0.13190290331840515f, kTanhP3 = -0.04440207779407501f;
+// Degree-2 fit of the same on |u| <= kTanhPoly2U (same method; relative error
+// 4.5e-7 evaluated in float32), one FMA fewer per score.
+constexpr float kTanhPoly2U = 0.25f;
+constexpr float kTanhQ0 = 0.9999995827674866f, kTanhQ1 = -0.33321908116340637f;
+constexpr float kTanhQ2 = 0.12841613590717316f;
 }  // namespace attn
 
 #ifndef ATTN_LDS_AHEAD
@@ -177,6 +182,15 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     const int n_tiles = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN - kt_begin : 0;
     const int wt_begin = w_hi > w_lo ? w_lo / BN : 0;
     const int wt_end = w_hi > w_lo ? (w_hi + BN - 1) / BN : 0;
+    // Order of the key tiles. With ALiBi under a causal mask the bias grows by
+    // slope * 64 per tile toward the diagonal (up to about 65 in exp2 units
+    // for the steepest head), so walking the keys forward would move the
+    // exponent reference, and rescale the output, on almost every tile; from
+    // the diagonal backward the row max is met first and rarely grows.
+    const bool rev = ALIBI && causal;
+    auto ktile = [&](int i) __attribute__((always_inline)) {   // key tile of step i
+        return rev ? kt_begin + n_tiles - 1 - i : kt_begin + i;
+    };
 
     const int row = wq0 + l32;
     const int doc_i = DOC ? docrow[min(row, Nq - 1)] : 0;
@@ -188,14 +202,19 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     // v = c x (exp2 units), P a degree-3 fit of tanh(u) / u on |u| <= 1/2
     // (relative error 6.2e-7 evaluated in float32), its coefficients rescaled
     // so that P is evaluated at v^2. Used for a tile when every raw score of
-    // the wave satisfies |x| <= tc_xmax.
+    // the wave satisfies |x| <= tc_xmax; when every |x| <= tq_xmax (|u| <= 1/4)
+    // the degree-2 fit instead.
     float tc1 = 0.f, tc2 = 0.f, tc3 = 0.f, tc_xmax = 0.f;
+    float tq1 = 0.f, tq2 = 0.f, tq_xmax = 0.f;   // the degree-2 form, |x| <= tq_xmax
     if (SOFTCAP) {
         const float k = 1.f / (cap_l2 * cap_l2);
         tc1 = kTanhP1 * k;
         tc2 = kTanhP2 * k * k;
         tc3 = kTanhP3 * k * k * k;
         tc_xmax = kTanhPolyU * p.softcap / p.scale;
+        tq1 = kTanhQ1 * k;
+        tq2 = kTanhQ2 * k * k;
+        tq_xmax = kTanhPoly2U * p.softcap / p.scale;
     }
 
     // ---- Q fragments (B operand of GEMM0): lane holds row l32, d = 16 s + 8 hh + 0..7
@@ -360,7 +379,15 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
             }
             a0 = max3_abs(a0, sacc[0][15], a1);
             a0 = max3_abs(a0, sacc[1][15], sacc[1][15]);
-            if (__builtin_amdgcn_ballot_w64(!(a0 <= tc_xmax)) == 0) {
+            if (__builtin_amdgcn_ballot_w64(!(a0 <= tq_xmax)) == 0) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = sacc[kb][r] * c, t = v * v;
+                        sacc[kb][r] = v * __builtin_fmaf(__builtin_fmaf(tq2, t, tq1), t, kTanhQ0);
+                    }
+            } else if (__builtin_amdgcn_ballot_w64(!(a0 <= tc_xmax)) == 0) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -480,11 +507,11 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     Copy copy;
     copy.init(wave, lane);
     auto tile_k = [&](int i) __attribute__((always_inline)) {
-        copy.template issue<false>(K, (kt_begin + i) * BN, Nk, lds_addr(kbuf(i)), wave);
+        copy.template issue<false>(K, ktile(i) * BN, Nk, lds_addr(kbuf(i)), wave);
     };
     auto tile_v = [&](int i) __attribute__((always_inline)) {
-        copy.template issue<true>(V, (kt_begin + i) * BN, Nk, lds_addr(vbuf(i)), wave);
-        if (DOC) issue_docs(docrow, (kt_begin + i) * BN, Nk, lds_addr(dbuf(i)), wave, lane);
+        copy.template issue<true>(V, ktile(i) * BN, Nk, lds_addr(vbuf(i)), wave);
+        if (DOC) issue_docs(docrow, ktile(i) * BN, Nk, lds_addr(dbuf(i)), wave, lane);
     };
 
     // ---------------------------------------------------------------- ping-pong loops
@@ -524,7 +551,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     // Iteration it over a tile of this wave's key range: softmax and GEMM1 of
     // tile it, GEMM0 of tile it + 1 (when it is also in the range).
     auto body = [&](int it, bool next) __attribute__((always_inline)) {
-        const int kt = kt_begin + it;
+        const int kt = ktile(it);
         if (group_b) barrier_and_copy(it + 1, !LATE_B);
         softmax(kt, dbuf(it));
         if (!group_b) barrier_and_copy(it + 1, !LATE_A);
@@ -542,8 +569,8 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     // this wave's tiles: [wb, we) relative to kt_begin
     int wb = n_tiles, we = n_tiles;
     if (wt_end > wt_begin) {
-        wb = wt_begin - kt_begin;
-        we = wt_end - kt_begin;
+        wb = rev ? kt_begin + n_tiles - wt_end : wt_begin - kt_begin;
+        we = rev ? kt_begin + n_tiles - wt_begin : wt_end - kt_begin;
     }
     if (n_tiles > 0) {
 #pragma unroll
