@@ -43,6 +43,8 @@ KERNEL_SOURCES = {"bf16": ["attn_fwd_bf16.hip", "fwd_common.h", "common.h", "fwd
                   "fp8": ["fp8.hip", "fwd_common.h", "common.h", "fwd_params.h"],
                   "f32": ["attn_fwd_f32.hip", "fwd_common.h", "common.h", "fwd_params.h"]}
 PROFILE_SUMMARY = {2: "profiles/fwd_bf16_causal_prefill_b4_h32_n4096_d128.md",
+                   3: "profiles/fwd_bf16_gqa_window_b2_h32x8_n16384_w4096_d128.md",
+                   4: "profiles/fwd_bf16_docs_softcap_alibi_b1_h16_n32768_d128.md",
                    5: "profiles/fwd_fp8_dense_b4_h16_n8192_d128.md",
                    6: "profiles/fwd_bf16_varlen_causal_t32768_h32x8_d128.md",
                    7: "profiles/decode_paged_b64_h32x8_d128_len1k-8k.md",

@@ -1,8 +1,9 @@
 """The kernels' gfx950 assembly has no uncovered matrix-core hazard.
 
 Compiles the forward kernels' sources to assembly with the library's own flags
-(device code only, on the CPU) and scans every kernel instantiation with
-``tests/isa_scan.py``. A positive control plants each hazard in a short
+(device code only, on the CPU), as built for libattn.so and with
+``-DATTN_SINGLE_STAGE`` as built for the single-stage debug library, and scans
+every kernel instantiation with ``tests/isa_scan.py``. A positive control plants each hazard in a short
 assembly listing and checks that the scan reports it.
 """
 import os
@@ -16,21 +17,22 @@ from tiled_attention_05_amd import build as B
 SOURCES = ["attn_fwd_bf16.hip", "fp8.hip"]
 
 
-def _asm(src, tmp_path):
+def _asm(src, tmp_path, defines=()):
     try:
         hipcc = B._hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
     out = tmp_path / (src + ".s")
-    cmd = [hipcc, *B.HIP_FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
+    cmd = [hipcc, *B.HIP_FLAGS, *defines, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     return out.read_text()
 
 
+@pytest.mark.parametrize("defines", [(), ("-DATTN_SINGLE_STAGE",)], ids=["pipelined", "single_stage"])
 @pytest.mark.parametrize("src", SOURCES)
-def test_no_uncovered_mfma_hazard(src, tmp_path):
-    ks = {k: v for k, v in isa_scan.kernels(_asm(src, tmp_path)).items() if "fwd_" in k}
+def test_no_uncovered_mfma_hazard(src, defines, tmp_path):
+    ks = {k: v for k, v in isa_scan.kernels(_asm(src, tmp_path, defines)).items() if "fwd_" in k}
     assert ks, "no forward kernel found in the assembly"
     bad = {k: isa_scan.scan(v) for k, v in ks.items()}
     bad = {k: v for k, v in bad.items() if v}

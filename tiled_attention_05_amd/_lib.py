@@ -9,6 +9,7 @@ built library every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -16,6 +17,8 @@ import os
 import torch
 
 PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# the same library with the forward kernels built -DATTN_SINGLE_STAGE (tests only)
+PATH_SINGLE_STAGE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_single_stage.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 F32, BF16, FP8_E4M3 = 0, 1, 2
@@ -41,44 +44,62 @@ def load():
     """Load the library once; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(PATH):
-            raise RuntimeError(f"{PATH} is missing; build it with `python -m tiled_attention_05_amd.build`")
-        lib = ctypes.CDLL(PATH)
-        lib.attn_fwd.restype = _i
-        lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _f, _vp,
-                                 _i, _vp]
-        lib.attn_fwd_varlen.restype = _i
-        lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _f, _vp,
-                                        _vp, _i, _vp]
-        lib.attn_fp8_buffer_bytes.restype = _sz
-        lib.attn_fp8_buffer_bytes.argtypes = [_i, _i, _i, _i]
-        lib.attn_fp8_prepare.restype = _i
-        lib.attn_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]
-        lib.attn_fp8_prepare_rope.restype = _i
-        lib.attn_fp8_prepare_rope.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
-                                              _vp]
-        lib.attn_decode_workspace_floats.restype = _sz
-        lib.attn_decode_workspace_floats.argtypes = [_i, _i, _i, _i]
-        lib.attn_decode_paged.restype = _i
-        lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
-                                          _i, _vp]
-        lib.attn_decode_paged_noalloc.restype = _i
-        lib.attn_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
-                                                  _i, _i, _vp]
-        lib.attn_bwd.restype = _i
-        lib.attn_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp]
-        lib.attn_block_mask_bytes.restype = _sz
-        lib.attn_block_mask_bytes.argtypes = [_i, _i, _i, _i, _i]
-        lib.attn_block_mask_build.restype = _i
-        lib.attn_block_mask_build.argtypes = [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp]
-        lib.attn_fwd_tile_kinds_bytes.restype = _sz
-        lib.attn_fwd_tile_kinds_bytes.argtypes = [_i, _i, _i]
-        lib.attn_fwd_tile_kinds.restype = _i
-        lib.attn_fwd_tile_kinds.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp]
-        lib.attn_status_string.restype = ctypes.c_char_p
-        lib.attn_status_string.argtypes = [_i]
-        _lib = lib
+        _lib = _open(PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def library(path):
+    """Route every call made inside the block through the library at path
+    (another build of the same C ABI, e.g. PATH_SINGLE_STAGE)."""
+    global _lib
+    saved = _lib
+    _lib = _open(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _open(path):
+    """Load the library at path and declare the C signatures of include/attn.h."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with `python -m tiled_attention_05_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.attn_fwd.restype = _i
+    lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _f, _vp,
+                             _i, _vp]
+    lib.attn_fwd_varlen.restype = _i
+    lib.attn_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _f, _vp,
+                                    _vp, _i, _vp]
+    lib.attn_fp8_buffer_bytes.restype = _sz
+    lib.attn_fp8_buffer_bytes.argtypes = [_i, _i, _i, _i]
+    lib.attn_fp8_prepare.restype = _i
+    lib.attn_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]
+    lib.attn_fp8_prepare_rope.restype = _i
+    lib.attn_fp8_prepare_rope.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp]
+    lib.attn_decode_workspace_floats.restype = _sz
+    lib.attn_decode_workspace_floats.argtypes = [_i, _i, _i, _i]
+    lib.attn_decode_paged.restype = _i
+    lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
+                                      _i, _vp]
+    lib.attn_decode_paged_noalloc.restype = _i
+    lib.attn_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                                              _i, _i, _vp]
+    lib.attn_bwd.restype = _i
+    lib.attn_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.attn_block_mask_bytes.restype = _sz
+    lib.attn_block_mask_bytes.argtypes = [_i, _i, _i, _i, _i]
+    lib.attn_block_mask_build.restype = _i
+    lib.attn_block_mask_build.argtypes = [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp]
+    lib.attn_fwd_tile_kinds_bytes.restype = _sz
+    lib.attn_fwd_tile_kinds_bytes.argtypes = [_i, _i, _i]
+    lib.attn_fwd_tile_kinds.restype = _i
+    lib.attn_fwd_tile_kinds.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [_i]
+    return lib
 
 
 def _ptr(t):

@@ -6,6 +6,13 @@ Every HIP source is compiled with packed-fp32 instruction selection disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host-only C ABI
 file is plain C++.  Objects go to ``_build/`` at the repository root and the
 shared library lands next to this file, where ``_lib.load()`` finds it.
+
+A second library, ``libattn_single_stage.so``, is linked from the same objects
+except the two forward kernels, which are compiled with ``-DATTN_SINGLE_STAGE``:
+one key/value tile in flight and every copy waited for as soon as it is
+issued. It exists for the tests only, which require its results to equal the
+pipelined library's bit for bit (a missing wait or a buffer reused too early
+shows up as a difference).
 """
 from __future__ import annotations
 
@@ -20,6 +27,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+LIB_SINGLE_STAGE = os.path.join(PKG, "libattn_single_stage.so")
+SINGLE_STAGE_SOURCES = ("attn_fwd_bf16.hip", "fp8.hip")   # the sources that read ATTN_SINGLE_STAGE
 ARCH = "gfx950"
 
 HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
@@ -39,8 +48,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src, hipcc, extra):
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+def _compile(src, hipcc, extra, tag=""):
+    obj = os.path.join(OBJ, os.path.basename(src) + tag + ".o")
     if src.endswith(".hip"):
         cmd = [hipcc, *HIP_FLAGS, *extra, "-c", src, "-o", obj]
     else:
@@ -51,21 +60,34 @@ def _compile(src, hipcc, extra):
     return obj
 
 
-def build(verbose: bool = True, extra=()) -> str:
-    """Compile every source and link libattn.so; returns its path."""
-    hipcc = _hipcc()
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(min(len(srcs), os.cpu_count() or 4, 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc, list(extra)), srcs))
-    tmp = LIB + ".tmp"
+def _link(hipcc, objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True, extra=(), single_stage: bool = True) -> str:
+    """Compile every source and link libattn.so (and, unless single_stage is
+    False, libattn_single_stage.so); returns the path of libattn.so."""
+    hipcc = _hipcc()
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    jobs = [(s, list(extra), "") for s in srcs]
+    if single_stage:
+        jobs += [(s, list(extra) + ["-DATTN_SINGLE_STAGE"], ".single_stage") for s in srcs
+                 if os.path.basename(s) in SINGLE_STAGE_SOURCES]
+    with ThreadPoolExecutor(min(len(jobs), os.cpu_count() or 4, 8)) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], hipcc, j[1], j[2]), jobs))
+    _link(hipcc, objs[:len(srcs)], LIB)
+    if single_stage:
+        alt = dict(zip((os.path.basename(s) for s, _, _ in jobs[len(srcs):]), objs[len(srcs):]))
+        _link(hipcc, [alt.get(os.path.basename(s), o) for s, o in zip(srcs, objs[:len(srcs)])], LIB_SINGLE_STAGE)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+        print(f"built {LIB}" + (f" and {os.path.basename(LIB_SINGLE_STAGE)}" if single_stage else "")
+              + f" from {len(srcs)} sources", file=sys.stderr)
     return LIB
 
 

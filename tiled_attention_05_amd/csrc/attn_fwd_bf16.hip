@@ -69,6 +69,15 @@ constexpr float kTanhQ0 = 0.9999995827674866f, kTanhQ1 = -0.33321908116340637f;
 constexpr float kTanhQ2 = 0.12841613590717316f;
 }  // namespace attn
 
+#ifdef ATTN_SINGLE_STAGE
+// Debug build: one key/value tile in flight, each copy waited for as soon as it
+// is issued, fragments read just before their product. The arithmetic is the
+// same as in the pipelined build, so the results must be equal bit for bit.
+#define ATTN_PREFETCH 1
+#define ATTN_LDS_AHEAD 1
+#define ATTN_LATE_COPY_A 0
+#define ATTN_LATE_COPY_B 0
+#endif
 #ifndef ATTN_LDS_AHEAD
 #define ATTN_LDS_AHEAD 4   // matrix fragments read from LDS ahead of their product
 #endif
@@ -528,6 +537,9 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
         if (i + PF < n_tiles) {
             tile_k(i + PF);
             tile_v(i + PF);
+#ifdef ATTN_SINGLE_STAGE
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+#endif
         }
     };
     auto barrier_and_copy = [&](int i, bool copy = true) __attribute__((always_inline)) {

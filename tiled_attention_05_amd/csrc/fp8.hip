@@ -281,7 +281,14 @@ template <bool RAGGED>
 __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     using T = Fp8Tile;
     constexpr int NW = 8, BM = NW * 32, D = 128;
-    constexpr int PF = 2, NKB = PF + 1, NVB = PF + 2;
+#ifdef ATTN_SINGLE_STAGE
+    // debug build: one tile in flight, each copy waited for as soon as it is
+    // issued; the arithmetic is unchanged, so the results must be equal bit for bit
+    constexpr int PF = 1;
+#else
+    constexpr int PF = 2;
+#endif
+    constexpr int NKB = PF + 1, NVB = PF + 2;
     constexpr float kTau = kFp8PShift;   // lazy-rescale threshold (log2 units)
     constexpr int KBUF = 2 * T::KBYTES;  // key tile: value codes, then residual codes
     constexpr int LOADS_PER_TILE = 3;    // copies per wave and tile: K value, K residual, V
@@ -551,11 +558,15 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
         if (i + PF < n_tiles) {
             tile_k(i + PF);
             tile_v(i + PF);
+#ifdef ATTN_SINGLE_STAGE
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+#endif
         }
     };
     auto barrier_and_copy = [&](int i, bool copy = true) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        if (i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
+        // tile i must have landed; with PF = 2 the copies of tile i + 1 may stay in flight
+        if (PF >= 2 && i + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | LOADS_PER_TILE);
         else __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     if (n_tiles > 0) {
         tile_k(0);
         tile_v(0);
-        if (n_tiles > 1) {
+        if (PF >= 2 && n_tiles > 1) {
             tile_k(1);
             tile_v(1);
         }
