@@ -209,20 +209,23 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     const float cap_in = SOFTCAP ? p.scale * 2.f * kLog2e / p.softcap : 0.f;
     // Soft-cap on small scores: cap tanh(v / cap) = v P((v / cap)^2) with
     // v = c x (exp2 units), P a degree-3 fit of tanh(u) / u on |u| <= 1/2
-    // (relative error 6.2e-7 evaluated in float32), its coefficients rescaled
-    // so that P is evaluated at v^2. Used for a tile when every raw score of
+    // (relative error 6.2e-7 evaluated in float32). The coefficients are
+    // rescaled so that x P'(x^2) gives the capped score straight from the raw
+    // one (P'(t) = c P(c^2 t / cap^2)). Used for a tile when every raw score of
     // the wave satisfies |x| <= tc_xmax; when every |x| <= tq_xmax (|u| <= 1/4)
     // the degree-2 fit instead.
-    float tc1 = 0.f, tc2 = 0.f, tc3 = 0.f, tc_xmax = 0.f;
-    float tq1 = 0.f, tq2 = 0.f, tq_xmax = 0.f;   // the degree-2 form, |x| <= tq_xmax
+    float tc0 = 0.f, tc1 = 0.f, tc2 = 0.f, tc3 = 0.f, tc_xmax = 0.f;
+    float tq0 = 0.f, tq1 = 0.f, tq2 = 0.f, tq_xmax = 0.f;   // the degree-2 form, |x| <= tq_xmax
     if (SOFTCAP) {
-        const float k = 1.f / (cap_l2 * cap_l2);
-        tc1 = kTanhP1 * k;
-        tc2 = kTanhP2 * k * k;
-        tc3 = kTanhP3 * k * k * k;
+        const float k = c * c / (cap_l2 * cap_l2);   // u^2 = k x^2
+        tc0 = kTanhP0 * c;
+        tc1 = kTanhP1 * k * c;
+        tc2 = kTanhP2 * k * k * c;
+        tc3 = kTanhP3 * k * k * k * c;
         tc_xmax = kTanhPolyU * p.softcap / p.scale;
-        tq1 = kTanhQ1 * k;
-        tq2 = kTanhQ2 * k * k;
+        tq0 = kTanhQ0 * c;
+        tq1 = kTanhQ1 * k * c;
+        tq2 = kTanhQ2 * k * k * c;
         tq_xmax = kTanhPoly2U * p.softcap / p.scale;
     }
 
@@ -359,8 +362,9 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     };
 
     // Score modifiers and / or the element mask, in place: the scores become
-    // exp2-unit values, -inf where the key is not allowed for the row.
-    auto prepare_scores = [&](bool full, int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
+    // exp2-unit values plus zoff (the same for all scores of the lane), -inf
+    // where the key is not allowed for the row.
+    auto prepare_scores = [&](bool full, int kt, const ATTN_LDS int* dl, float zoff) __attribute__((always_inline)) {
         const int j0 = kt * BN;
         int dk[2][16];
         if (DOC && !full) {
@@ -393,17 +397,17 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float v = sacc[kb][r] * c, t = v * v;
-                        sacc[kb][r] = v * __builtin_fmaf(__builtin_fmaf(tq2, t, tq1), t, kTanhQ0);
+                        const float x = sacc[kb][r], t = x * x;
+                        sacc[kb][r] = __builtin_fmaf(x, __builtin_fmaf(__builtin_fmaf(tq2, t, tq1), t, tq0), zoff);
                     }
             } else if (__builtin_amdgcn_ballot_w64(!(a0 <= tc_xmax)) == 0) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float v = sacc[kb][r] * c, t = v * v;
-                        sacc[kb][r] = v * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(tc3, t, tc2), t, tc1), t,
-                                                         kTanhP0);
+                        const float x = sacc[kb][r], t = x * x;
+                        sacc[kb][r] = __builtin_fmaf(
+                            x, __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(tc3, t, tc2), t, tc1), t, tc0), zoff);
                     }
             } else {
 #pragma unroll
@@ -412,7 +416,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                     for (int r = 0; r < 16; ++r) {
                         // cap - 2 cap / (exp(2 x / cap) + 1)
                         const float e = fast_exp2(sacc[kb][r] * cap_in);
-                        sacc[kb][r] = cap_l2 - 2.f * cap_l2 * fast_rcp(e + 1.f);
+                        sacc[kb][r] = __builtin_fmaf(-2.f * cap_l2, fast_rcp(e + 1.f), cap_l2 + zoff);
                     }
             }
         }
@@ -428,7 +432,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                 for (int r = 0; r < 16; ++r) {
                     if ((r & 3) == 0) pin(sacc[kb]);   // four elements at a time
                     const float x = sacc[kb][r];
-                    float y = SOFTCAP ? x : x * c;
+                    float y = SOFTCAP ? x : ALIBI ? __builtin_fmaf(x, c, zoff) : x * c;
                     if (ALIBI) y = __builtin_fmaf((float)(32 * kb + 8 * (r >> 2) + (r & 3)), slope_l2, y);
                     sacc[kb][r] = y;
                 }
@@ -440,7 +444,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                     const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
                     if ((r & 3) == 0) pin(sacc[kb]);
                     const float x = sacc[kb][r];
-                    float y = SOFTCAP ? x : x * c;
+                    float y = SOFTCAP ? x : ALIBI ? __builtin_fmaf(x, c, zoff) : x * c;
                     if (ALIBI) y = __builtin_fmaf((float)(32 * kb + 8 * (r >> 2) + (r & 3)), slope_l2, y);
                     bool ok = jl <= jl_hi && jl >= jl_lo;
                     if (DOC) ok &= dk[kb][r] == doc_i;
@@ -456,7 +460,14 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     auto softmax = [&](int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
         const bool full = is_full(kt, dl);
         const bool pre = MODS || !full || !(c > 0.f);
-        if (pre) prepare_scores(full, kt, dl);
+        // lane part of the ALiBi bias (see prepare_scores), 0 without ALiBi
+        const float alibi_lane = ALIBI ? slope_l2 * (float)(kt * BN + 4 * hh - row) : 0.f;
+        // With score modifiers, once every row of the wave has a reference the
+        // scores are prepared relative to it (the modifier's last FMA adds
+        // alibi_lane - m), so that the exponent needs no argument instruction
+        // on tiles where no row's reference moves.
+        const bool rel = MODS && __builtin_amdgcn_ballot_w64(!(m > kNoMax)) == 0;
+        if (pre) prepare_scores(full, kt, dl, rel ? alibi_lane - m : 0.f);
         const float ce = pre ? 1.f : c;
         float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
 #pragma unroll
@@ -465,25 +476,43 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
             a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
         }
         a0 = max3(a0, sacc[0][15], max2(a1, sacc[1][15]));
-        // lane part of the ALiBi bias (see prepare_scores), 0 without ALiBi
-        const float alibi_lane = ALIBI ? slope_l2 * (float)(kt * BN + 4 * hh - row) : 0.f;
-        const float mx = xhalf_max(a0 + alibi_lane) * ce;
-        const float mn = max2(m, mx);
-        const bool need = mn > m + kLazyTau;
-        const float alpha = need ? fast_exp2(m - mn) : 1.f;
-        m = need ? mn : m;
-        const float mneg = alibi_lane - m;
+        bool need;
+        float alpha, ce2, mneg;   // p = exp2(s ce2 + mneg)
+        if (rel) {
+            const float mx = xhalf_max(a0);   // the tile's max over the reference
+            need = mx > kLazyTau;
+            alpha = need ? fast_exp2(-mx) : 1.f;
+            m = need ? m + mx : m;
+            ce2 = 1.f;
+            mneg = need ? -mx : 0.f;
+        } else {
+            const float mx = xhalf_max(a0 + alibi_lane) * ce;
+            const float mn = max2(m, mx);
+            need = mn > m + kLazyTau;
+            alpha = need ? fast_exp2(m - mn) : 1.f;
+            m = need ? mn : m;
+            ce2 = ce;
+            mneg = alibi_lane - m;
+        }
+        // relative scores and no reference moved: the exponent of the score itself
+        const bool plain = rel && __builtin_amdgcn_ballot_w64(need) == 0;
         float ls0 = -0.f, ls1 = -0.f, ls2 = -0.f, ls3 = -0.f;   // -0 + p folds to p
+        auto exps = [&](auto arg) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][r], ce, mneg));
-                const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r + 1], ce, mneg));
-                if (r & 2) { ls2 += p0; ls3 += p1; } else { ls0 += p0; ls1 += p1; }
-                pf[kb][r >> 3][(r & 7)] = (__bf16)p0;
-                pf[kb][r >> 3][(r & 7) + 1] = (__bf16)p1;
-            }
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(arg(sacc[kb][r]));
+                    const float p1 = fast_exp2(arg(sacc[kb][r + 1]));
+                    if (r & 2) { ls2 += p0; ls3 += p1; } else { ls0 += p0; ls1 += p1; }
+                    pf[kb][r >> 3][(r & 7)] = (__bf16)p0;
+                    pf[kb][r >> 3][(r & 7) + 1] = (__bf16)p1;
+                }
+        };
+        if (plain)
+            exps([](float x) __attribute__((always_inline)) { return x; });
+        else
+            exps([&](float x) __attribute__((always_inline)) { return __builtin_fmaf(x, ce2, mneg); });
         // P is complete here; GEMM1 reads it only after the wait states below
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
