@@ -425,30 +425,41 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
         // 4 hh): the first part is added here, one FMA with a literal per
         // score; the second, the same for all scores of the lane, is folded
         // into the row max and the exponent reference (alibi_lane).
-        if (full) {   // no element mask
+        // The same pass on every tile, then the element mask on partial ones,
+        // both in place (separate full / partial versions of the first pass
+        // made the compiler merge their results through register copies).
+        if (MODS) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if ((r & 3) == 0) pin(sacc[kb]);   // four elements at a time
+                    const int jc = 32 * kb + 8 * (r >> 2) + (r & 3);
                     const float x = sacc[kb][r];
-                    float y = SOFTCAP ? x : ALIBI ? __builtin_fmaf(x, c, zoff) : x * c;
-                    if (ALIBI) y = __builtin_fmaf((float)(32 * kb + 8 * (r >> 2) + (r & 3)), slope_l2, y);
+                    float y = SOFTCAP ? x : __builtin_fmaf(x, c, zoff);
+                    if (ALIBI && jc != 0) y = __builtin_fmaf((float)jc, slope_l2, y);
                     sacc[kb][r] = y;
                 }
-        } else {
+        }
+        if (!full) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int jl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);   // key within tile
                     if ((r & 3) == 0) pin(sacc[kb]);
-                    const float x = sacc[kb][r];
-                    float y = SOFTCAP ? x : ALIBI ? __builtin_fmaf(x, c, zoff) : x * c;
-                    if (ALIBI) y = __builtin_fmaf((float)(32 * kb + 8 * (r >> 2) + (r & 3)), slope_l2, y);
+                    const float y = MODS ? sacc[kb][r] : sacc[kb][r] * c;
                     bool ok = jl <= jl_hi && jl >= jl_lo;
                     if (DOC) ok &= dk[kb][r] == doc_i;
                     sacc[kb][r] = ok ? y : -INFINITY;
+                }
+        } else if (!MODS) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if ((r & 3) == 0) pin(sacc[kb]);
+                    sacc[kb][r] *= c;
                 }
         }
     };
