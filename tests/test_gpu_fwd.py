@@ -89,6 +89,25 @@ def test_softcap_polynomial_and_exact_tiles():
     _check(w, x, "softcap both forms")
 
 
+def test_softcap_every_form():
+    """Soft-cap 50 with the 32-row blocks of Q scaled by 1, 2.3, 4.5 and 8 in
+    turn: the kernel picks its form per wave tile (32 rows x 64 keys) from the
+    largest |scale q.k| of the tile -- degree-1 polynomial up to cap/8,
+    degree-2 up to cap/4, degree-3 up to cap/2, the exact form beyond -- and
+    every form is taken by some tile of this launch."""
+    w = I.WORKLOADS[2].shrink(B=1, Hq=2, Hkv=2, N=512, mask=0, softcap=50.0)
+    x = I.inputs(w, seed=9)
+    f = torch.tensor([1.0, 2.3, 4.5, 8.0]).repeat(w.N // 128).repeat_interleave(32)
+    x["q"] = (x["q"].float() * f[None, None, :, None]).to(x["q"].dtype)
+    s = (x["q"].float() @ x["k"].float().transpose(-1, -2)) * w.scale
+    tmax = s.abs().reshape(w.B, w.Hq, w.N // 32, 32, w.N // 64, 64).amax(dim=(3, 5))
+    bands = [int(((tmax > lo) & (tmax <= hi)).sum()) for lo, hi in
+             ((0, 6.25), (6.25, 12.5), (12.5, 25.0), (25.0, float("inf")))]
+    print(f"[softcap forms] wave tiles per form (degree 1, 2, 3, exact): {bands}", flush=True)
+    assert all(b > 0 for b in bands)
+    _check(w, x, "softcap every form")
+
+
 @pytest.mark.parametrize("N", [1, 5, 63, 64, 65, 255, 257])
 @pytest.mark.parametrize("mask", [0, C])
 def test_short_sequences(N, mask):

@@ -67,6 +67,10 @@ constexpr float kTanhP2 = 0.13190290331840515f, kTanhP3 = -0.04440207779407501f;
 constexpr float kTanhPoly2U = 0.25f;
 constexpr float kTanhQ0 = 0.9999995827674866f, kTanhQ1 = -0.33321908116340637f;
 constexpr float kTanhQ2 = 0.12841613590717316f;
+// Degree-1 fit of the same on |u| <= kTanhPoly1U (same method; relative error
+// 4.2e-6 evaluated in float32), for the small scores most tiles hold.
+constexpr float kTanhPoly1U = 0.125f;
+constexpr float kTanhL0 = 0.9999959468841553f, kTanhL1 = -0.33126187324523926f;
 }  // namespace attn
 
 #ifdef ATTN_SINGLE_STAGE
@@ -213,9 +217,11 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     // rescaled so that x P'(x^2) gives the capped score straight from the raw
     // one (P'(t) = c P(c^2 t / cap^2)). Used for a tile when every raw score of
     // the wave satisfies |x| <= tc_xmax; when every |x| <= tq_xmax (|u| <= 1/4)
-    // the degree-2 fit instead.
+    // the degree-2 fit instead, when every |x| <= tl_xmax (|u| <= 1/8) the
+    // degree-1 fit.
     float tc0 = 0.f, tc1 = 0.f, tc2 = 0.f, tc3 = 0.f, tc_xmax = 0.f;
     float tq0 = 0.f, tq1 = 0.f, tq2 = 0.f, tq_xmax = 0.f;   // the degree-2 form, |x| <= tq_xmax
+    float tl0 = 0.f, tl1 = 0.f, tl_xmax = 0.f;              // the degree-1 form, |x| <= tl_xmax
     if (SOFTCAP) {
         const float k = c * c / (cap_l2 * cap_l2);   // u^2 = k x^2
         tc0 = kTanhP0 * c;
@@ -227,6 +233,9 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
         tq1 = kTanhQ1 * k * c;
         tq2 = kTanhQ2 * k * k * c;
         tq_xmax = kTanhPoly2U * p.softcap / p.scale;
+        tl0 = kTanhL0 * c;
+        tl1 = kTanhL1 * k * c;
+        tl_xmax = kTanhPoly1U * p.softcap / p.scale;
     }
 
     // ---- Q fragments (B operand of GEMM0): lane holds row l32, d = 16 s + 8 hh + 0..7
@@ -392,7 +401,15 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
             }
             a0 = max3_abs(a0, sacc[0][15], a1);
             a0 = max3_abs(a0, sacc[1][15], sacc[1][15]);
-            if (__builtin_amdgcn_ballot_w64(!(a0 <= tq_xmax)) == 0) {
+            if (__builtin_amdgcn_ballot_w64(!(a0 <= tl_xmax)) == 0) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x = sacc[kb][r], t = x * x;
+                        sacc[kb][r] = __builtin_fmaf(x, __builtin_fmaf(tl1, t, tl0), zoff);
+                    }
+            } else if (__builtin_amdgcn_ballot_w64(!(a0 <= tq_xmax)) == 0) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
