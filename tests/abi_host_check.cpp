@@ -32,6 +32,7 @@ hipError_t launch_fwd_plan(int, int, int, int, int, const int32_t*, int8_t*, hip
     return hipSuccess;
 }
 hipError_t launch_seq_ids(const int32_t*, int, int, int32_t*, hipStream_t) { ++launches; return hipSuccess; }
+hipError_t launch_varlen_tiles(const int32_t*, int, int, int32_t*, int, hipStream_t) { ++launches; return hipSuccess; }
 hipError_t launch_decode(const void*, const void*, const void*, const int32_t*, const int32_t*, void*, float*, int,
                          int, int, int, float, int, float*, hipStream_t) {
     ++launches;
@@ -109,12 +110,17 @@ int main() {
                     ATTN_FP8_E4M3, nullptr),
            ATTN_ERR_UNSUPPORTED, 0);
     // varlen, prepare, block mask, plan, decode, backward
-    // with ATTN_LOG the forward copies the document ids to the host: with no
-    // device that copy fails, after the sequence-index launch, as ATTN_ERR_HIP
+    // bf16 varlen: the tile list, then the forward; fp32 varlen: the sequence
+    // index, then the document-mask forward -- with ATTN_LOG that forward
+    // copies the document ids to the host, which with no device fails, after
+    // the sequence-index launch, as ATTN_ERR_HIP
     const char* lg = std::getenv("ATTN_LOG");
     const bool log = lg && lg[0] && lg[0] != '0';
     EXPECT(attn_fwd_varlen(P, P, P, P, nullptr, D, 3, 100, 4, 2, 128, 0.1f, ATTN_MASK_CAUSAL, 0, 0.f, nullptr,
                            (int32_t*)P, ATTN_BF16, nullptr),
+           ATTN_OK, 2);
+    EXPECT(attn_fwd_varlen(P, P, P, P, nullptr, D, 3, 100, 4, 2, 64, 0.1f, ATTN_MASK_CAUSAL, 0, 0.f, nullptr,
+                           (int32_t*)P, ATTN_F32, nullptr),
            log ? ATTN_ERR_HIP : ATTN_OK, log ? 1 : 2);
     EXPECT(attn_fwd_varlen(P, P, P, P, nullptr, D, 0, 100, 4, 2, 128, 0.1f, 0, 0, 0.f, nullptr, (int32_t*)P, 1,
                            nullptr),

@@ -15,6 +15,23 @@ pytestmark = pytest.mark.gpu
 C, W = I.MASK_CAUSAL, I.MASK_WINDOW
 
 
+def _tile_list(lengths, bm=256):
+    """The per-sequence tile list the bf16 path writes into the workspace, or
+    None where the host picks the document path: the first packed row of each
+    (sequence, 256-row tile), tile index descending, then sequences by tile
+    count descending (lower index first), padded with -1 to
+    ceil(total / 256) + num_seqs entries."""
+    total, ns = sum(lengths), len(lengths)
+    n_list = -(-total // bm) + ns
+    if ns > 4096 or -(-total // bm) > 4096 or n_list > total:
+        return None
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    nt = [-(-n // bm) for n in lengths]
+    order = sorted(range(ns), key=lambda s: (-nt[s], s))
+    items = [int(cu[s] + t * bm) for t in reversed(range(max(nt))) for s in order if nt[s] > t]
+    return items + [-1] * (n_list - len(items))
+
+
 def _pack(lengths, Hq, Hkv, d, dtype, seed):
     T = sum(lengths)
     g = torch.Generator("cpu").manual_seed(seed)
@@ -32,6 +49,9 @@ CASES = [
     ("one long", [3000], 2, 2, 128, torch.bfloat16, C, 0, 0.0, False),
     ("many short", [17] * 40 + [3] * 20, 2, 2, 128, torch.bfloat16, C, 0, 0.0, False),
     ("fp32", [5, 200, 77], 2, 2, 64, torch.float32, C, 0, 0.0, False),
+    # more tile-list entries than workspace entries: bf16 takes the document path
+    ("one-token sequences (document path)", [1] * 10, 2, 2, 128, torch.bfloat16, C, 0, 0.0, False),
+    ("empty sequences (document path)", [0, 0, 3, 0, 0, 0], 2, 1, 128, torch.bfloat16, C, 0, 5.0, True),
 ]
 
 
@@ -49,9 +69,14 @@ def test_varlen_matches_oracle(label, lengths, Hq, Hkv, d, dtype, mask, window, 
                              workspace=ws)
     torch.cuda.synchronize()
     O, L = A.attention_varlen(q, k, v, cu, scale, mask, window, softcap, slopes)
-    # the workspace holds each token's sequence index (integer work: bit-exact)
-    ids = np.searchsorted(cu.numpy(), np.arange(q.shape[1]), side="right") - 1
-    assert np.array_equal(ws.cpu().numpy(), ids)
+    # the workspace holds the bf16 path's tile list, else each token's
+    # sequence index (integer work: bit-exact)
+    tiles = _tile_list(lengths) if dtype == torch.bfloat16 else None
+    if tiles is not None:
+        assert ws[:len(tiles)].cpu().tolist() == tiles
+    else:
+        ids = np.searchsorted(cu.numpy(), np.arange(q.shape[1]), side="right") - 1
+        assert np.array_equal(ws.cpu().numpy(), ids)
     kw = dict(max_abs=1e-4, mean_abs=1e-5, lse_tol=1e-5) if dtype == torch.float32 else {}
     assert_close(o[None], lse[None], O[None], L[None], label=f"varlen {label}", **kw)
 
@@ -78,11 +103,30 @@ def test_varlen_workload_sampled_rows():
             assert_close(o[h, idx], lse[h, idx], O, L, label=f"varlen workload h={h} seq@{a}")
 
 
-def test_varlen_equals_fwd_with_document_ids():
-    """The varlen entry point and attn_fwd with the matching document ids run
-    the same kernel: bit-identical outputs."""
+@pytest.mark.parametrize("mask,softcap,alibi", [(C, 0.0, False), (C | W, 30.0, True), (0, 0.0, False)])
+def test_varlen_bf16_equals_fwd_per_sequence(mask, softcap, alibi):
+    """bf16 varlen tiles every sequence on its own: each sequence's rows are
+    bit-identical to attn_fwd on that sequence alone."""
+    lengths = [100, 1, 700, 0, 63, 256, 257]
+    q, k, v, cu = _pack(lengths, 4, 2, 128, torch.bfloat16, seed=3)
+    sl = I.alibi_slopes(4).cuda() if alibi else None
+    o1, l1 = _lib.fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu.cuda(), mask=mask, window=50, softcap=softcap,
+                             alibi_slopes=sl)
+    for a, b in zip(cu[:-1].tolist(), cu[1:].tolist()):
+        if b == a:
+            continue
+        o2, l2 = _lib.fwd(q[None, :, a:b].contiguous().cuda(), k[None, :, a:b].contiguous().cuda(),
+                          v[None, :, a:b].contiguous().cuda(), mask=mask, window=50, softcap=softcap,
+                          alibi_slopes=sl)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[:, a:b], o2[0]) and torch.equal(l1[:, a:b], l2[0]), (a, b)
+
+
+def test_varlen_fp32_equals_fwd_with_document_ids():
+    """fp32 varlen and attn_fwd with the matching document ids run the same
+    kernel: bit-identical outputs."""
     lengths = [100, 1, 400, 63]
-    q, k, v, cu = _pack(lengths, 2, 2, 128, torch.bfloat16, seed=3)
+    q, k, v, cu = _pack(lengths, 2, 2, 64, torch.float32, seed=3)
     o1, l1 = _lib.fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu.cuda(), mask=C)
     ids = torch.repeat_interleave(torch.arange(len(lengths), dtype=torch.int32), torch.tensor(lengths))
     o2, l2 = _lib.fwd(q[None].cuda(), k[None].cuda(), v[None].cuda(), mask=C | I.MASK_DOC,

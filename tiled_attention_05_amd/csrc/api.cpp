@@ -25,6 +25,8 @@ hipError_t launch_block_mask(int B, int Nq, int Nk, int mask, int window, const 
 hipError_t launch_fwd_plan(int B, int Nq, int Nk, int mask, int window, const int32_t* doc, int8_t* kinds,
                            hipStream_t st);
 hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* ids, hipStream_t st);
+hipError_t launch_varlen_tiles(const int32_t* cu, int n_seq, int bm, int32_t* items, int n_list, hipStream_t st);
+constexpr int kVarlenMaxSeqs = 4096, kVarlenMaxTiles = 4096;   // as in varlen.hip
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* table, const int32_t* lens,
                          void* o, float* lse, int B, int Hq, int Hkv, int max_blocks, float scale, int splits,
                          float* workspace, hipStream_t st);
@@ -245,8 +247,33 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
         for (int s2 = 1; s2 <= num_seqs; ++s2) ok &= cu[s2] >= cu[s2 - 1];
         if (!ok) return ATTN_ERR_INVALID_ARG;
     }
+    // bf16: each sequence tiled on its own (256-row query tiles that never
+    // straddle two sequences), when the tile list fits the workspace; else
+    // (and for fp32) the document mask over the concatenation.
+    constexpr int kBM = 256;
+    const long long n_list = (total + kBM - 1) / kBM + (long long)num_seqs;
+    const bool per_seq = dtype == ATTN_BF16 && num_seqs <= attn::kVarlenMaxSeqs &&
+                         (total + kBM - 1) / kBM <= attn::kVarlenMaxTiles && n_list <= total;
     if (log_enabled())
-        std::fprintf(stderr, "[attn] fwd_varlen num_seqs=%d total=%d\n", num_seqs, total);
+        std::fprintf(stderr, "[attn] fwd_varlen num_seqs=%d total=%d tiling=%s\n", num_seqs, total,
+                     per_seq ? "per-sequence" : "document-mask");
+    if (per_seq) {
+        if (const int r = hip_status(attn::launch_varlen_tiles(cu_seqlens, num_seqs, kBM, workspace, (int)n_list,
+                                                               (hipStream_t)stream)))
+            return r;
+        attn::FwdParams p{};
+        p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+        p.slopes = alibi_slopes;
+        p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.Nq = total; p.Nk = total;
+        p.group = Hq / Hkv;
+        p.mask = mask_kind;
+        p.window = (mask_kind & ATTN_MASK_WINDOW) ? window : 0;
+        p.scale = scale;
+        p.scale_log2 = scale * 1.4426950408889634f;
+        p.softcap = softcap;
+        p.items = workspace; p.cu = cu_seqlens; p.n_seq = num_seqs; p.n_list = (int)n_list;
+        return hip_status(attn::launch_fwd_bf16(p, d, (hipStream_t)stream));
+    }
     if (const int r = hip_status(attn::launch_seq_ids(cu_seqlens, num_seqs, total, workspace, (hipStream_t)stream)))
         return r;
     return fwd_launch(q, k, v, o, lse, 1, Hq, Hkv, total, total, d, scale, mask, window, workspace, softcap,

@@ -168,14 +168,33 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
         bh = (u / p.Hkv) * p.Hq + (u % p.Hkv) * p.group + q;
     }
     const int b = bh / p.Hq, h = bh % p.Hq, g = h / p.group;
-    const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+    int Nq = p.Nq, Nk = p.Nk;
+    // Packed variable-length batch tiled per sequence: the k-th heaviest
+    // query tile is entry k of the item list (its first packed row); rows,
+    // keys and pointers are then those of its sequence alone. Offsets are
+    // clamped into the packed length, so any list stays in bounds.
+    int row0 = 0;
+    if (!DOC && p.items) {
+        const int r = p.items[p.n_qt - 1 - qt];
+        if (r < 0) return;   // list padding: the whole workgroup leaves before any barrier
+        const int s = min(max(wave_search<true>(p.cu, p.n_seq + 1, r, lane) - 1, 0), p.n_seq - 1);
+        const int s0 = min(max(p.cu[s], 0), p.Nq), s1 = min(max(p.cu[s + 1], s0), p.Nq);
+        if (r < s0 || r >= s1) return;   // only with offsets that do not partition the batch
+        Nq = Nk = s1 - s0;
+        qt = (r - s0) / BM;
+        row0 = s0;
+    }
+    const int off = Nk - Nq;
     const bool causal = p.mask & kMaskCausal, windowed = p.mask & kMaskWindow;
     const int W = p.window;
     const int q0 = qt * BM;
 
-    const __bf16* Q = (const __bf16*)p.q + (size_t)(b * p.Hq + h) * Nq * D;
-    const __bf16* K = (const __bf16*)p.k + (size_t)(b * p.Hkv + g) * Nk * D;
-    const __bf16* V = (const __bf16*)p.v + (size_t)(b * p.Hkv + g) * Nk * D;
+    // row 0 of this (batch, head) in Q / O (and LSE), and in K / V
+    const size_t qbase = (size_t)(b * p.Hq + h) * p.Nq + row0;
+    const size_t kbase = (size_t)(b * p.Hkv + g) * p.Nk + row0;
+    const __bf16* Q = (const __bf16*)p.q + qbase * D;
+    const __bf16* K = (const __bf16*)p.k + kbase * D;
+    const __bf16* V = (const __bf16*)p.v + kbase * D;
     const int32_t* docrow = DOC ? p.doc + (size_t)b * Nk : nullptr;
 
     // ---- this wave's rows and its contiguous key range [w_lo, w_hi)
@@ -668,7 +687,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     mfma_guard();
 #pragma unroll
     for (int t = 0; t < DT; ++t) pin_a(o[t]);
-    __bf16* O = (__bf16*)p.o + (size_t)(b * p.Hq + h) * Nq * D;
+    __bf16* O = (__bf16*)p.o + qbase * D;
     const float lt = xhalf_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row < Nq) {
@@ -683,7 +702,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                 *(bf16x4*)(orow + 32 * t + 8 * gq) = w;
             }
         if (p.lse && hh == 0)
-            p.lse[(size_t)(b * p.Hq + h) * Nq + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+            p.lse[qbase + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     }
 }
 
@@ -772,7 +791,7 @@ template <int D, bool SC, bool AL, bool DC>
 static hipError_t launch_bf16_inst(const FwdParams& p0, hipStream_t st) {
     FwdParams p = p0;
     constexpr int BM = 256;
-    p.n_qt = (p.Nq + BM - 1) / BM;
+    p.n_qt = p.items ? p.n_list : (p.Nq + BM - 1) / BM;
     p.n_bh = p.B * p.Hq;
     // Head groups per XCD: as many heads as fill two rounds of its resident
     // workgroups (32 CUs, one workgroup each; one round measured slower),

@@ -25,6 +25,14 @@ struct FwdParams {
     int n_bh;               // B * Hq
     int npad;               // fp8: token count padded to the scale tile
     int xgrp;               // bf16: heads per XCD in one dispatch group, 0 = plain order
+    // bf16 packed variable-length batch tiled per sequence (B = 1, Nq = Nk =
+    // the packed length, tensors [H][total][d]): items[k] is the first packed
+    // row of the k-th heaviest query tile (-1: list padding), cu the sequence
+    // offsets [n_seq + 1]; nullptr otherwise
+    const int32_t* items;
+    const int32_t* cu;
+    int n_seq;
+    int n_list;             // entries of items
 };
 
 }  // namespace attn

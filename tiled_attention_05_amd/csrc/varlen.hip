@@ -4,8 +4,9 @@
 // [cu[s], cu[s + 1]) of one packed sequence, and a token attends only within
 // its own sequence -- the document mask of "FlexAttention de PyTorch avec
 // FlashAttention-4 change la donne" (opening section) over the concatenation.
-// This kernel writes the per-token sequence index that the forward's document
-// path reads.
+// seq_ids_kernel writes the per-token sequence index that the forward's
+// document path reads; varlen_tiles_kernel the per-sequence tile list of the
+// bf16 path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,6 +30,76 @@ __global__ __launch_bounds__(256) void seq_ids_kernel(const int32_t* __restrict_
 hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* ids, hipStream_t st) {
     hipLaunchKernelGGL(seq_ids_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, cu, num_seqs,
                        total, ids);
+    return hipGetLastError();
+}
+
+// Per-sequence tiling of a packed batch for the bf16 forward: one list entry
+// per (sequence s, query tile t of bm rows), the entry being the tile's first
+// packed row cu[s] + t bm. Heavy first: tile index t descending (a later tile
+// attends to more keys), and for one t the sequences with more tiles first
+// (ties: lower index first). Sequences are ranked by their tile count; the
+// sequences with more than t tiles then hold ranks 0 .. cnt[t] - 1, so tile
+// (s, t) goes to off[t] + rank(s) with off[t] the number of tiles of larger
+// index. Entries past the tile count are -1. One workgroup; n_seq <=
+// kVarlenMaxSeqs and every sequence at most kVarlenMaxTiles tiles (the caller
+// checks both; longer ones are cut, and no write leaves the n_list entries).
+constexpr int kVarlenMaxSeqs = 4096, kVarlenMaxTiles = 4096;
+
+__global__ __launch_bounds__(1024) void varlen_tiles_kernel(const int32_t* __restrict__ cu, int n_seq, int bm,
+                                                            int32_t* __restrict__ items, int n_list) {
+    __shared__ int nt[kVarlenMaxSeqs];     // tiles of sequence s
+    __shared__ int rk[kVarlenMaxSeqs];     // rank of s by tile count, descending
+    __shared__ int cnt[kVarlenMaxTiles];   // sequences with more than t tiles, then off[t]
+    __shared__ int part[1024];
+    const int tid = threadIdx.x;
+    for (int s = tid; s < n_seq; s += 1024)
+        nt[s] = min((max(cu[s + 1] - cu[s], 0) + bm - 1) / bm, kVarlenMaxTiles);
+    for (int t = tid; t < kVarlenMaxTiles; t += 1024) cnt[t] = 0;
+    __syncthreads();
+    for (int s = tid; s < n_seq; s += 1024) {
+        const int n = nt[s];
+        int r = 0;
+        for (int c = 0; c < n_seq; ++c) r += (nt[c] > n || (nt[c] == n && c < s)) ? 1 : 0;
+        rk[s] = r;
+        for (int t = 0; t < n; ++t) atomicAdd(&cnt[t], 1);
+    }
+    __syncthreads();
+    // off[t] = sum of cnt[t'] over t' > t: an exclusive scan of cnt read from
+    // the top index down, 4 entries per thread
+    constexpr int PER = kVarlenMaxTiles / 1024;
+    int a[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        a[i] = cnt[kVarlenMaxTiles - 1 - (PER * tid + i)];
+        sum += a[i];
+    }
+    part[tid] = sum;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int x = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += x;
+        __syncthreads();
+    }
+    int run = part[tid] - sum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        cnt[kVarlenMaxTiles - 1 - (PER * tid + i)] = run;
+        run += a[i];
+    }
+    const int n_tiles = part[1023];
+    __syncthreads();
+    for (int s = tid; s < n_seq; s += 1024)
+        for (int t = 0; t < nt[s]; ++t) {
+            const int at = cnt[t] + rk[s];
+            if (at < n_list) items[at] = cu[s] + t * bm;
+        }
+    for (int i = n_tiles + tid; i < n_list; i += 1024) items[i] = -1;
+}
+
+hipError_t launch_varlen_tiles(const int32_t* cu, int n_seq, int bm, int32_t* items, int n_list, hipStream_t st) {
+    if (n_seq < 1 || n_seq > kVarlenMaxSeqs || bm < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(1024), 0, st, cu, n_seq, bm, items, n_list);
     return hipGetLastError();
 }
 
