@@ -128,9 +128,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *              optionally | ATTN_MASK_WINDOW (with window W as in attn_fwd).
  * softcap, alibi_slopes, scale, d, Hq, Hkv: as attn_fwd (ALiBi distances are
  *              within a sequence).
- * workspace  : device int32 [total], caller-owned; overwritten with each
- *              token's sequence index before the forward runs (the library
- *              allocates nothing). Must not alias another argument.
+ * workspace  : device int32 [total], caller-owned scratch, overwritten before
+ *              the forward runs (the library allocates nothing); must not
+ *              alias another argument. ATTN_BF16, when ceil(total / 256) +
+ *              num_seqs <= total, num_seqs <= 4096 and total <= 4096 * 256:
+ *              each sequence is tiled on its own, and the first
+ *              ceil(total / 256) + num_seqs entries receive the list of its
+ *              256-row query tiles (first packed row of each tile; tile index
+ *              descending, then sequences by tile count descending, lower
+ *              index first; -1 past the last tile). Otherwise, and for
+ *              ATTN_F32: each token's sequence index, and the document-mask
+ *              forward over the concatenation. The two paths group keys
+ *              into tiles differently, so their results agree up to rounding.
  * dtype      : ATTN_F32 or ATTN_BF16.
  * Errors     : ATTN_ERR_INVALID_ARG for NULL q/k/v/o/cu_seqlens/workspace,
  *              num_seqs < 1, total < 1, mask bits other than CAUSAL / WINDOW,
