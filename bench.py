@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tiled_attention_05_amd", "csrc")
 # kernel sources whose hash keys the measured HBM traffic of a profile summary
 KERNEL_SOURCES = {"bf16": ["attn_fwd_bf16.hip", "fwd_common.h", "common.h", "fwd_params.h"],
+                  "varlen": ["attn_fwd_bf16.hip", "varlen.hip", "fwd_common.h", "common.h", "fwd_params.h"],
                   "decode": ["decode.hip", "fwd_common.h", "common.h"],
                   "bwd": ["bwd.hip", "fwd_common.h", "common.h"],
                   "fp8": ["fp8.hip", "fwd_common.h", "common.h", "fwd_params.h"],
@@ -358,7 +359,7 @@ def main():
         extra = {"prepare_ms": round(ms_prep, 4), "prepare_GBps": round(prep_bytes / ms_prep / 1e6, 1),
                  "prepare_rope_ms": round(ms_rope, 4), "prepare_rope_GBps": round(rope_bytes / ms_rope / 1e6, 1),
                  "end_to_end_tflops": round(fl / ((ms_prep + ms_kernel) * 1e-3) / 1e12, 2)}
-    traffic, sclk = measured_profile(args.workload, dt)
+    traffic, sclk = measured_profile(args.workload, "varlen" if w.extra.get("varlen") else dt)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -134,9 +134,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *              num_seqs <= total, num_seqs <= 4096 and total <= 4096 * 256:
  *              each sequence is tiled on its own, and the first
  *              ceil(total / 256) + num_seqs entries receive the list of its
- *              256-row query tiles (first packed row of each tile; tile index
- *              descending, then sequences by tile count descending, lower
- *              index first; -1 past the last tile). Otherwise, and for
+ *              256-row query tiles (first packed row of each tile;
+ *              sequences by tile count descending, lower index first, each
+ *              sequence's tiles from its last to its first; -1 past the last
+ *              tile). Otherwise, and for
  *              ATTN_F32: each token's sequence index, and the document-mask
  *              forward over the concatenation. The two paths group keys
  *              into tiles differently, so their results agree up to rounding.

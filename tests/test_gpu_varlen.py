@@ -18,9 +18,9 @@ C, W = I.MASK_CAUSAL, I.MASK_WINDOW
 def _tile_list(lengths, bm=256):
     """The per-sequence tile list the bf16 path writes into the workspace, or
     None where the host picks the document path: the first packed row of each
-    (sequence, 256-row tile), tile index descending, then sequences by tile
-    count descending (lower index first), padded with -1 to
-    ceil(total / 256) + num_seqs entries."""
+    (sequence, 256-row tile), sequences by tile count descending (lower index
+    first), each sequence's tiles from its last to its first, padded with -1
+    to ceil(total / 256) + num_seqs entries."""
     total, ns = sum(lengths), len(lengths)
     n_list = -(-total // bm) + ns
     if ns > 4096 or -(-total // bm) > 4096 or n_list > total:
@@ -28,7 +28,7 @@ def _tile_list(lengths, bm=256):
     cu = np.concatenate([[0], np.cumsum(lengths)])
     nt = [-(-n // bm) for n in lengths]
     order = sorted(range(ns), key=lambda s: (-nt[s], s))
-    items = [int(cu[s] + t * bm) for t in reversed(range(max(nt))) for s in order if nt[s] > t]
+    items = [int(cu[s] + t * bm) for s in order for t in reversed(range(nt[s]))]
     return items + [-1] * (n_list - len(items))
 
 

@@ -35,42 +35,41 @@ hipError_t launch_seq_ids(const int32_t* cu, int num_seqs, int total, int32_t* i
 
 // Per-sequence tiling of a packed batch for the bf16 forward: one list entry
 // per (sequence s, query tile t of bm rows), the entry being the tile's first
-// packed row cu[s] + t bm. Heavy first: tile index t descending (a later tile
-// attends to more keys), and for one t the sequences with more tiles first
-// (ties: lower index first). Sequences are ranked by their tile count; the
-// sequences with more than t tiles then hold ranks 0 .. cnt[t] - 1, so tile
-// (s, t) goes to off[t] + rank(s) with off[t] the number of tiles of larger
-// index. Entries past the tile count are -1. One workgroup; n_seq <=
-// kVarlenMaxSeqs and every sequence at most kVarlenMaxTiles tiles (the caller
-// checks both; longer ones are cut, and no write leaves the n_list entries).
+// packed row cu[s] + t bm. Order: sequences by tile count, descending (ties:
+// lower index first), and within a sequence its tiles from the last (the
+// heaviest: it attends to the most keys) to the first. The tiles in flight at
+// once then come from one or two sequences and share their keys and values in
+// the L2 of each XCD, and the grid ends on the light tiles of the shortest
+// sequences. Entries past the tile count are -1. One workgroup; n_seq <=
+// kVarlenMaxSeqs (the caller checks it); tile counts are cut at
+// kVarlenMaxTiles, and no write leaves the n_list entries.
 constexpr int kVarlenMaxSeqs = 4096, kVarlenMaxTiles = 4096;
 
 __global__ __launch_bounds__(1024) void varlen_tiles_kernel(const int32_t* __restrict__ cu, int n_seq, int bm,
                                                             int32_t* __restrict__ items, int n_list) {
-    __shared__ int nt[kVarlenMaxSeqs];     // tiles of sequence s
-    __shared__ int rk[kVarlenMaxSeqs];     // rank of s by tile count, descending
-    __shared__ int cnt[kVarlenMaxTiles];   // sequences with more than t tiles, then off[t]
+    __shared__ int nt[kVarlenMaxSeqs];    // tiles of sequence s
+    __shared__ int rk[kVarlenMaxSeqs];    // rank of s by tile count, descending
+    __shared__ int at[kVarlenMaxSeqs];    // tiles of the sequence of rank r, then its first list entry
     __shared__ int part[1024];
     const int tid = threadIdx.x;
     for (int s = tid; s < n_seq; s += 1024)
         nt[s] = min((max(cu[s + 1] - cu[s], 0) + bm - 1) / bm, kVarlenMaxTiles);
-    for (int t = tid; t < kVarlenMaxTiles; t += 1024) cnt[t] = 0;
+    for (int r = tid; r < kVarlenMaxSeqs; r += 1024) at[r] = 0;
     __syncthreads();
     for (int s = tid; s < n_seq; s += 1024) {
         const int n = nt[s];
         int r = 0;
         for (int c = 0; c < n_seq; ++c) r += (nt[c] > n || (nt[c] == n && c < s)) ? 1 : 0;
         rk[s] = r;
-        for (int t = 0; t < n; ++t) atomicAdd(&cnt[t], 1);
+        at[r] = n;   // ranks are a permutation of 0 .. n_seq - 1
     }
     __syncthreads();
-    // off[t] = sum of cnt[t'] over t' > t: an exclusive scan of cnt read from
-    // the top index down, 4 entries per thread
-    constexpr int PER = kVarlenMaxTiles / 1024;
+    // first entry of rank r: exclusive scan of the tile counts in rank order
+    constexpr int PER = kVarlenMaxSeqs / 1024;
     int a[PER], sum = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        a[i] = cnt[kVarlenMaxTiles - 1 - (PER * tid + i)];
+        a[i] = at[PER * tid + i];
         sum += a[i];
     }
     part[tid] = sum;
@@ -84,16 +83,18 @@ __global__ __launch_bounds__(1024) void varlen_tiles_kernel(const int32_t* __res
     int run = part[tid] - sum;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        cnt[kVarlenMaxTiles - 1 - (PER * tid + i)] = run;
+        at[PER * tid + i] = run;
         run += a[i];
     }
     const int n_tiles = part[1023];
     __syncthreads();
-    for (int s = tid; s < n_seq; s += 1024)
-        for (int t = 0; t < nt[s]; ++t) {
-            const int at = cnt[t] + rk[s];
-            if (at < n_list) items[at] = cu[s] + t * bm;
+    for (int s = tid; s < n_seq; s += 1024) {
+        const int first = at[rk[s]], n = nt[s];
+        for (int t = 0; t < n; ++t) {
+            const int e = first + (n - 1 - t);
+            if (e < n_list) items[e] = cu[s] + t * bm;
         }
+    }
     for (int i = n_tiles + tid; i < n_list; i += 1024) items[i] = -1;
 }
 
