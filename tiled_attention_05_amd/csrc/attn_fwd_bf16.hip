@@ -720,8 +720,16 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 template <int D, bool SOFTCAP, bool ALIBI, bool DOC>
 __global__ __launch_bounds__(512) void fwd_bf16_persistent_kernel(FwdParams p) {
     __shared__ Bf16Lds<D, DOC> sm;
-    const int n_items = p.n_qt * p.n_bh;
-    for (int wid = blockIdx.x; wid < n_items; wid += gridDim.x) {
+    const int n_items = p.n_qt * p.n_bh, G = gridDim.x, w = blockIdx.x;
+    // Snake order: in odd rounds the items are taken in reverse within this
+    // workgroup's XCD class (w % 8; item r G + j runs on XCD j % 8 as in the
+    // plain launch), so a workgroup that took a heavy item takes a light one
+    // next and the workgroups' totals stay close.
+    const bool snake = G % 8 == 0;
+    for (int r = 0; r * G < n_items; ++r) {
+        const int j = (snake && (r & 1)) ? (G / 8 - 1 - w / 8) * 8 + w % 8 : w;
+        const int wid = r * G + j;
+        if (wid >= n_items) continue;
         fwd_bf16_item<D, SOFTCAP, ALIBI, DOC>(p, wid, sm);
         __syncthreads();
     }
