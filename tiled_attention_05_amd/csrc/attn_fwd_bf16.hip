@@ -111,7 +111,7 @@ struct Bf16Lds {
 
 // One work item (query tile qt of one (batch, head)) of the bf16 forward,
 // run by the whole workgroup; wid is the item's index in the launch order.
-template <int D, bool SOFTCAP, bool ALIBI, bool DOC>
+template <int D, bool SOFTCAP, bool ALIBI, bool DOC, bool PERSIST = false>
 __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p, int wid,
                                                              Bf16Lds<D, DOC>& sm) {
     using T = Tile<D>;
@@ -690,20 +690,46 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     __bf16* O = (__bf16*)p.o + qbase * D;
     const float lt = xhalf_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (row < Nq) {
-        __bf16* orow = O + (size_t)row * D + 4 * hh;
+    // The output goes to HBM through this wave's own half of a tile buffer:
+    // in registers each lane holds a quarter-row of d values (4 of every 8),
+    // which stored directly writes 16-byte pieces of 32 rows per instruction;
+    // read back row-wise, each store writes whole contiguous rows (the wave's
+    // 32 rows are one contiguous block of O). After the last barrier no wave
+    // reads the key buffers or any value buffer but the last tile's.
+    static_assert(2 * 32 * T::ROW_BYTES <= T::BYTES && NKB + NVB - 1 >= NW / 2, "output staging space");
+    int sbuf = wave / 2;
+    if (n_tiles > 0 && sbuf >= NKB + (n_tiles - 1) % NVB) ++sbuf;
+    ATTN_LDS char* stage = lds + sbuf * T::BYTES + (wave & 1) * (32 * T::ROW_BYTES);
+    // In a persistent workgroup the lane-only offsets are computed here, not
+    // hoisted out of its item loop (where they would be kept in scratch).
+    int ln = lane;
+    if (PERSIST) pin(ln);
+    asm volatile("" ::: "memory");
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                bf16x4 w;
+        for (int gq = 0; gq < 4; ++gq) {
+            bf16x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[t][4 * gq + e] * inv);
-                *(bf16x4*)(orow + 32 * t + 8 * gq) = w;
-            }
-        if (p.lse && hh == 0)
-            p.lse[qbase + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[t][4 * gq + e] * inv);
+            // d = 32 t + 8 gq + 4 hh + e: chunk 4 t + gq of row l32, bytes 8 hh ..
+            const int r = ln & 31;
+            const int ch = (4 * t + gq) ^ T::swz_k(r);
+            *(ATTN_LDS bf16x4*)(stage + r * T::ROW_BYTES + ch * 16 + 8 * (ln >> 5)) = w;
+        }
+    asm volatile("" ::: "memory");
+    {
+        constexpr int RPI = 64 / T::CPR;   // rows per 16-byte-per-lane instruction
+        const int rr = ln / T::CPR, cc = ln % T::CPR;
+#pragma unroll
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int r = k * RPI + rr;
+            const bf16x8 x = *(const ATTN_LDS bf16x8*)(stage + r * T::ROW_BYTES + ((cc ^ T::swz_k(r)) * 16));
+            if (wq0 + r < Nq) *(bf16x8*)(O + (size_t)(wq0 + r) * D + cc * 8) = x;
+        }
     }
+    if (row < Nq && p.lse && hh == 0)
+        p.lse[qbase + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
 }
 
 // One workgroup per work item (the grid is every item of the launch).
@@ -730,7 +756,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_persistent_kernel(FwdParams p) {
         const int j = (snake && (r & 1)) ? (G / 8 - 1 - w / 8) * 8 + w % 8 : w;
         const int wid = r * G + j;
         if (wid >= n_items) continue;
-        fwd_bf16_item<D, SOFTCAP, ALIBI, DOC>(p, wid, sm);
+        fwd_bf16_item<D, SOFTCAP, ALIBI, DOC, true>(p, wid, sm);
         __syncthreads();
     }
 }

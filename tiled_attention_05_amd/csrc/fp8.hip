@@ -292,7 +292,13 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     constexpr float kTau = kFp8PShift;   // lazy-rescale threshold (log2 units)
     constexpr int KBUF = 2 * T::KBYTES;  // key tile: value codes, then residual codes
     constexpr int LOADS_PER_TILE = 3;    // copies per wave and tile: K value, K residual, V
-    __shared__ __attribute__((aligned(1024))) char tiles_lds[NKB * KBUF + NVB * T::VBYTES];
+    // The epilogue stages each wave's 32 output rows (8 KiB) in a slot of this
+    // space no wave reads any more: at least 9 slots, one of which may still
+    // hold the last value tile.
+    constexpr int kTileSpace = NKB * KBUF + NVB * T::VBYTES;
+    constexpr int kSlot = 32 * D * 2;
+    static_assert(KBUF % kSlot == 0 && T::VBYTES == kSlot, "output staging slots");
+    __shared__ __attribute__((aligned(1024))) char tiles_lds[kTileSpace > 9 * kSlot ? kTileSpace : 9 * kSlot];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -609,20 +615,40 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
     for (int t = 0; t < 4; ++t) pin_a(o[t]);
     const float lt = xhalf_sum(l);
     const float inv = lt > 0.f ? svmax / (exp2f(kFp8PShift) * lt) : 0.f;
-    if (row < N) {
-        __bf16* orow = (__bf16*)p.o + (bhq * N + row) * D + 4 * hh;
+    // Output through LDS so that each store writes whole contiguous rows (a
+    // lane holds 4 of every 8 d values of its row; the wave's 32 rows are one
+    // contiguous block of O). 8 KiB slots: the key buffers first, then the
+    // value buffers; after the last barrier only the last tile's value buffer
+    // is still read, and the wave skips its slot.
+    int slot = wave;
+    if (n_tiles > 0 && slot >= NKB * KBUF / kSlot + (n_tiles - 1) % NVB) ++slot;
+    ATTN_LDS char* stage = (ATTN_LDS char*)tiles_lds + slot * kSlot;
+    asm volatile("" ::: "memory");
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                bf16x4 w;
+        for (int gq = 0; gq < 4; ++gq) {
+            bf16x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[t][4 * gq + e] * inv);
-                *(bf16x4*)(orow + 32 * t + 8 * gq) = w;
-            }
-        if (p.lse && hh == 0)
-            p.lse[bhq * N + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[t][4 * gq + e] * inv);
+            // d = 32 t + 8 gq + 4 hh + e: 16-byte chunk 4 t + gq of row l32,
+            // XOR-swizzled by the row so the 32 rows spread over the banks
+            const int ch = (4 * t + gq) ^ (l32 & 15);
+            *(ATTN_LDS bf16x4*)(stage + l32 * (2 * D) + ch * 16 + 8 * hh) = w;
+        }
+    asm volatile("" ::: "memory");
+    {
+        __bf16* O = (__bf16*)p.o + (bhq * N + wq0) * D;
+        const int rr = lane >> 4, cc = lane & 15;   // 4 rows of 16 chunks per instruction
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int r = 4 * k + rr;
+            const bf16x8 x = *(const ATTN_LDS bf16x8*)(stage + r * (2 * D) + ((cc ^ (r & 15)) * 16));
+            if (wq0 + r < N) *(bf16x8*)(O + (size_t)r * D + cc * 8) = x;
+        }
     }
+    if (row < N && p.lse && hh == 0)
+        p.lse[bhq * N + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
 }
 
 template __global__ void fwd_fp8_kernel<false>(FwdParams);
