@@ -158,6 +158,15 @@ __device__ __forceinline__ void store_rows(__bf16* head, int r0, int N, int lane
         }
 }
 
+// LDS of a gradient workgroup: two buffers of two 32-row chunk tiles (dK / dV:
+// Q and dO; dQ: K and V), each wave's own V block (dK / dV) and the chunk's LSE
+// and D values (dK / dV). 65 KB: two workgroups fit a CU.
+struct BwdLds {
+    __attribute__((aligned(1024))) char tiles[2][2][kBC * Tile<kBD>::ROW_BYTES];
+    __attribute__((aligned(1024))) char vblk[4][kBC * Tile<kBD>::ROW_BYTES];
+    __attribute__((aligned(16))) float stat[2][2 * kBC];
+};
+
 // dK, dV: one wave per (batch, key/value head, 32-key block), looping over
 // the query chunks of every query head of the group. The 4 waves of a
 // workgroup own 4 consecutive key blocks of one head, so they need the same
@@ -168,13 +177,12 @@ __device__ __forceinline__ void store_rows(__bf16* head, int r0, int N, int lane
 // chunks are fully masked and add exact zeros. The next chunk's tiles are
 // requested before the current chunk is computed (two LDS buffer sets, one
 // barrier per chunk); the loop has no load the compiler counts. Two
-// workgroups per CU (two waves per SIMD, 256 registers each: a few values are
-// reloaded from scratch per chunk) hide the latency of each wave's serial
-// chain S -> P -> dV, dK about 1.35x better than one wave per SIMD with
-// everything in registers.
-__device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid) {
-    __shared__ __attribute__((aligned(1024))) char lds[2][2][kBC * Tile<kBD>::ROW_BYTES];   // buffer, Q / dO
-    __shared__ __attribute__((aligned(16))) float stat[2][2 * kBC];   // buffer: LSE then D of the chunk
+// workgroups per CU (two waves per SIMD, 256 registers each; the wave's K
+// block in registers, its V block in LDS) hide the latency of each wave's
+// serial chain S -> P -> dV, dK about 1.35x better than one wave per SIMD.
+__device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid, BwdLds& sm) {
+    auto& lds = sm.tiles;   // [buffer][Q, dO]
+    auto& stat = sm.stat;   // [buffer]: LSE then D of the chunk
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nkb = (p.N + kBC - 1) / kBC, nkg = (nkb + 3) / 4;
@@ -187,9 +195,21 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid) {
     const int l32 = lane & 31, hh = lane >> 5;
     const int j0 = kb * kBC;
     const size_t kvh = ((size_t)b * p.Hkv + g) * p.N * kBD;
-    bf16x8 kf[8], vf[8];
+    bf16x8 kf[8];
     row_frags(p.k + kvh, j0, p.N, lane, kf);   // B operand of S = Q K^T: column = key
-    row_frags(p.v + kvh, j0, p.N, lane, vf);   // B operand of dP = dO V^T
+    // The V block (B operand of dP = dO V^T) stays in this wave's LDS, read
+    // each chunk: held in registers it pushed the loop past the 256-register
+    // cap (values reloaded from scratch every chunk). Chunk c of row r at
+    // c ^ (r mod 16), so the 16 rows of a 16-byte row read hit 16 bank groups.
+    ATTN_LDS char* vb = (ATTN_LDS char*)sm.vblk[wave];
+    {
+        using T = Tile<kBD>;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {   // 4 rows of 16 chunks per copy
+            const int r = 4 * i + (lane >> 4), pc = lane & 15;
+            dma16(p.v + kvh + (size_t)min(j0 + r, p.N - 1) * kBD + 8 * (pc ^ T::swz_k(r)), lds_addr(vb + i * 1024));
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no compiler-counted load stays pending into the loop
     int ofs[4];
     tr_offsets(lane, ofs);
@@ -222,7 +242,11 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid) {
         for (int st = 0; st < 8; ++st) s = mfma_bf16(af[st], kf[st], s);
         lds_row_frags((const ATTN_LDS char*)lds[buf][1], lane, af);
 #pragma unroll
-        for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], vf[st], dp);
+        for (int st = 0; st < 8; ++st) {
+            using T = Tile<kBD>;
+            const bf16x8 vf = *(const ATTN_LDS bf16x8*)(vb + l32 * T::ROW_BYTES + (((2 * st + hh) ^ T::swz_k(l32)) << 4));
+            dp = mfma_bf16(af[st], vf, dp);
+        }
         bf16x8 pk[2], sk[2];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -260,8 +284,8 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid) {
 // last query block still copies and meets the barriers, and stores nothing);
 // under a causal mask the group runs to the last chunk its last block sees,
 // the chunks beyond a block's diagonal being fully masked (exact zeros).
-__device__ __forceinline__ void dq_block(const BwdParams& p, int bid) {
-    __shared__ __attribute__((aligned(1024))) char lds[2][2][kBC * Tile<kBD>::ROW_BYTES];   // buffer, K / V
+__device__ __forceinline__ void dq_block(const BwdParams& p, int bid, BwdLds& sm) {
+    auto& lds = sm.tiles;   // [buffer][K, V]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nqb = (p.N + kBC - 1) / kBC, nqg = (nqb + 3) / 4;
@@ -335,14 +359,15 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int bid) {
 // dK/dV and dQ need only the inputs and D, not each other: one grid holds the
 // dK/dV workgroups first and the dQ workgroups after them, so the dQ work
 // fills the CUs the end of the dK/dV part leaves idle. Two workgroups per CU
-// (two waves per SIMD, 256 registers each: dK/dV reloads a few values from
-// scratch per chunk) hide the latency of each wave's serial product chain.
+// (two waves per SIMD, 256 registers each) hide the latency of each wave's
+// serial product chain.
 // The dK/dV part is padded to a multiple of 8 workgroups, so that workgroup
 // n_kv + w of the dQ part runs on the XCD w would (round-robin dispatch).
 __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
+    __shared__ BwdLds sm;
     const int bid = blockIdx.x;
-    if (bid < p.n_kv) dkdv_block(p, bid);
-    else dq_block(p, bid - p.n_kv);
+    if (bid < p.n_kv) dkdv_block(p, bid, sm);
+    else dq_block(p, bid - p.n_kv, sm);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
