@@ -85,8 +85,13 @@ __device__ __forceinline__ void tr_offsets(int lane, int ofs[4]) {
 }
 
 // Rows r0 .. r0 + 31 of one head (row-major [N][128], rows clamped to N - 1)
-// into an LDS tile shared by the 4 waves of a workgroup, swizzled for the
-// transposed reads: wave w copies the 4 rows of slots i = 2 w, 2 w + 1 of 8.
+// into an LDS tile shared by the 4 waves of a workgroup: wave w copies the 4
+// rows of slots i = 2 w, 2 w + 1 of 8. A tile read transposed (by itself or
+// also row-wise) takes the prefill kernel's V swizzle (chunk c of row r at
+// c ^ 4 (r mod 4)); a tile read only row-wise (ROWS) chunk c ^ (r mod 16),
+// in which the 16 rows of a quarter-wave's 16-byte reads hit 16 bank groups
+// instead of 4.
+template <bool ROWS = false>
 __device__ __forceinline__ void tile_part_to_lds(const __bf16* head, int r0, int N, unsigned base, int lane,
                                                  int wave) {
     using T = Tile<kBD>;
@@ -94,7 +99,7 @@ __device__ __forceinline__ void tile_part_to_lds(const __bf16* head, int r0, int
     for (int k = 0; k < 2; ++k) {
         const int i = 2 * wave + k;
         const int slot = i * 64 + lane, r = slot >> 4, pc = slot & 15;
-        const __bf16* src = head + (size_t)min(r0 + r, N - 1) * kBD + 8 * (pc ^ T::swz_v(r));
+        const __bf16* src = head + (size_t)min(r0 + r, N - 1) * kBD + 8 * (pc ^ (ROWS ? T::swz_k(r) : T::swz_v(r)));
         dma16(src, base + i * 1024);
     }
 }
@@ -116,13 +121,15 @@ __device__ __forceinline__ void row_frags(const __bf16* head, int r0, int N, int
 }
 
 // Row fragments (A or B operand: row l32 of the tile, dims 16 s + 8 hh + 0..7)
-// read from an LDS tile in the swizzled layout of tile_part_to_lds.
+// read from an LDS tile in the layout (ROWS or not) of tile_part_to_lds.
+template <bool ROWS = false>
 __device__ __forceinline__ void lds_row_frags(const ATTN_LDS char* tile, int lane, bf16x8 f[8]) {
     using T = Tile<kBD>;
     const int r = lane & 31, hh = lane >> 5;
     const ATTN_LDS char* rp = tile + r * T::ROW_BYTES;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) f[s] = *(const ATTN_LDS bf16x8*)(rp + (((2 * s + hh) ^ T::swz_v(r)) << 4));
+    for (int s = 0; s < 8; ++s)
+        f[s] = *(const ATTN_LDS bf16x8*)(rp + (((2 * s + hh) ^ (ROWS ? T::swz_k(r) : T::swz_v(r))) << 4));
 }
 
 // Product of a tile read transposed from LDS (A: 32 d-rows x 16 tile rows, per
@@ -316,21 +323,22 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int bid, BwdLds& sm
 
     auto issue = [&](int kc, int buf) __attribute__((always_inline)) {
         tile_part_to_lds(p.k + kvh, kc * kBC, p.N, lds_addr((ATTN_LDS char*)lds[buf][0]), lane, wave);
-        tile_part_to_lds(p.v + kvh, kc * kBC, p.N, lds_addr((ATTN_LDS char*)lds[buf][1]), lane, wave);
+        tile_part_to_lds<true>(p.v + kvh, kc * kBC, p.N, lds_addr((ATTN_LDS char*)lds[buf][1]), lane, wave);
     };
     auto compute = [&](int kc, int buf) __attribute__((always_inline)) {
         const int j0 = kc * kBC;
         // every (query, key) pair of the chunk allowed (see the dK / dV kernel)
         const bool full = i0 + kBC <= p.N && j0 + kBC <= p.N && (!p.causal || j0 + kBC - 1 <= i0);
         // S^T = K Q^T, dP^T = V dO^T: lane = query, registers = keys 8 (r / 4) + 4 hh + r % 4
-        bf16x8 af[8];
+        // both fragment sets requested before the products (the registers are there)
+        bf16x8 kr[8], vr[8];
         f32x16 s = f32x16{}, dp = f32x16{};
-        lds_row_frags((const ATTN_LDS char*)lds[buf][0], lane, af);
+        lds_row_frags((const ATTN_LDS char*)lds[buf][0], lane, kr);
+        lds_row_frags<true>((const ATTN_LDS char*)lds[buf][1], lane, vr);
 #pragma unroll
-        for (int st = 0; st < 8; ++st) s = mfma_bf16(af[st], qf[st], s);
-        lds_row_frags((const ATTN_LDS char*)lds[buf][1], lane, af);
+        for (int st = 0; st < 8; ++st) s = mfma_bf16(kr[st], qf[st], s);
 #pragma unroll
-        for (int st = 0; st < 8; ++st) dp = mfma_bf16(af[st], df[st], dp);
+        for (int st = 0; st < 8; ++st) dp = mfma_bf16(vr[st], df[st], dp);
         bf16x8 sk[2];
         auto probs = [&](auto mask_c) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_c)::value;
