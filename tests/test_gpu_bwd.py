@@ -86,3 +86,28 @@ def test_bwd_full_workload_sampled_heads():
         _close(dq[s], dQ, f"dQ b={b} h={h}")
         _close(dk[s], dK, f"dK b={b} h={h}")
         _close(dv[s], dV, f"dV b={b} h={h}")
+
+
+def test_bwd_seeded_sweep():
+    """24 seeded random shapes (batch, GQA ratio, ragged lengths, dense or
+    causal) against the float64 backward oracle to the bar above."""
+    import random
+    rng = random.Random(8)
+    for c in range(24):
+        hkv = rng.choice([1, 2, 4])
+        B, Hq, N, mask = rng.choice([1, 2]), hkv * rng.choice([1, 2, 4]), rng.choice([1, 31, 33, 128, 255, 400, 700]), \
+            rng.choice([0, 1])
+        print(f"[case] bwd sweep {c}: B={B} Hq={Hq} Hkv={hkv} N={N} mask={mask}", flush=True)
+        g = torch.Generator("cpu").manual_seed(500 + c)
+        q = torch.randn(B, Hq, N, 128, generator=g).to(torch.bfloat16)
+        k = torch.randn(B, hkv, N, 128, generator=g).to(torch.bfloat16)
+        v = torch.randn(B, hkv, N, 128, generator=g).to(torch.bfloat16)
+        do = torch.randn(B, Hq, N, 128, generator=g).to(torch.bfloat16)
+        qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+        o, lse = _lib.fwd(qd, kd, vd, mask=mask)
+        dq, dk, dv = _lib.bwd(qd, kd, vd, o, dod, lse, mask=mask)
+        torch.cuda.synchronize()
+        dQ, dK, dV = A.attention_backward(q, k, v, do, 128 ** -0.5, mask)
+        _close(dq, dQ, f"sweep {c} dQ")
+        _close(dk, dK, f"sweep {c} dK")
+        _close(dv, dV, f"sweep {c} dV")
