@@ -643,7 +643,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
         if (group_b) barrier_and_copy(it + 1, !LATE_B);
         softmax(kt, dbuf(it));
         if (!group_b) barrier_and_copy(it + 1, !LATE_A);
-        mfma_guard();   // P was written by vector code just before
+        operand_guard();   // P was written by vector code just before
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             pin(pf[kb][0]);

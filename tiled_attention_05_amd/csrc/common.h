@@ -124,6 +124,13 @@ __device__ __forceinline__ void mfma_fp8_a(f32x16& c, i32x8 a, i32x8 b) {     //
 __device__ __forceinline__ void mfma_guard() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
+// 4 wait states: more than the two instructions that must separate a vector
+// write of a register from a matrix instruction reading it as its A or B
+// operand (the reverse direction, a result read by vector code, takes
+// mfma_guard()). Values written before it are re-pinned after it, as there.
+__device__ __forceinline__ void operand_guard() {
+    asm volatile("s_nop 3" ::: "memory");
+}
 // Pins a value at this point of the instruction stream (an empty volatile
 // statement that reads and rewrites it), so work placed around it stays there.
 template <typename T>

@@ -582,7 +582,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(FwdParams p) {
         if (group_b) barrier_and_copy(it + 1, false);
         softmax(it);
         if (!group_b) barrier_and_copy(it + 1, false);
-        mfma_guard();   // P was written by vector code just before
+        operand_guard();   // P was written by vector code just before
         pin(pf);
         gemm1(vbuf(it));
         if (next) gemm0(kbuf(it + 1));
