@@ -204,7 +204,6 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     KeyRange kr{INT_MAX, INT_MIN, 0, 0};
     if (wave_active) kr = rows_key_range<DOC>(wq0, wq1, Nk, off, p.mask, W, docrow, lane);
     const int w_lo = kr.lo, w_hi = kr.hi;
-    const int dq0 = kr.dq0;
     if (lane == 0) { range_lds[wave][0] = w_lo; range_lds[wave][1] = w_hi; }
     __syncthreads();
     int kv_lo = INT_MAX, kv_hi = INT_MIN;

@@ -17,7 +17,7 @@ constexpr int kBmMax = 4096;
 
 __global__ void block_mask_clear(int32_t* flags) { *flags = 0; }
 
-__global__ __launch_bounds__(256) void block_mask_kernel(int B, int Nq, int Nk, int mask, int window,
+__global__ __launch_bounds__(256) void block_mask_kernel(int Nq, int Nk, int mask, int window,
                                                          const int32_t* doc, int bm, int bn,
                                                          int8_t* kinds, int32_t* counts,
                                                          int32_t* flags) {
@@ -73,7 +73,7 @@ hipError_t launch_block_mask(int B, int Nq, int Nk, int mask, int window, const 
     hipLaunchKernelGGL(block_mask_clear, dim3(1), dim3(1), 0, st, flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(block_mask_kernel, dim3((unsigned)(B * nqt)), dim3(256), 0, st, B, Nq, Nk, mask,
+    hipLaunchKernelGGL(block_mask_kernel, dim3((unsigned)(B * nqt)), dim3(256), 0, st, Nq, Nk, mask,
                        window, doc, bm, bn, kinds, counts, flags);
     return hipGetLastError();
 }
