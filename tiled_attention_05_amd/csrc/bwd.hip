@@ -12,10 +12,13 @@
 //
 // Products are 32x32x16 bf16 MFMAs (A: lane l holds row l % 32, k = 8 (l / 32)
 // + 0..7; B: column l % 32; C: lane l, register r holds row 8 (r / 4) +
-// 4 (l / 32) + r % 4, column l % 32). Operands read row-wise come straight from
-// global memory; operands needed transposed (Q^T, dO^T, K^T) go through a
-// per-wave LDS tile in the prefill kernel's swizzled layout and its transposed
-// reads, and the probabilities are packed in the matching permuted order.
+// 4 (l / 32) + r % 4, column l % 32). A wave's own block is read once: into
+// registers (K for dK / dV, Q and dO for dQ) or into the wave's part of LDS
+// (V for dK / dV). The streamed chunks (Q and dO for dK / dV, K and V for dQ)
+// go through LDS tiles shared by the workgroup's 4 waves, read row-wise (16-byte
+// reads) and, where an operand is needed transposed (Q^T, dO^T, K^T), with the
+// transposed reads of the prefill kernel's V layout; the probabilities are
+// packed in the matching permuted order.
 #include <climits>
 #include <type_traits>
 
