@@ -151,6 +151,28 @@ __device__ __forceinline__ void tr_gemm(const ATTN_LDS char* tile, const int ofs
         }
 }
 
+// The fragments of tr_gemm, all requested at once (f[4 u + t]), and its
+// products from them: for a caller with registers to hold the 8 fragments, so
+// that their reads overlap its vector work.
+__device__ __forceinline__ void tr_frags(const ATTN_LDS char* tile, const int ofs[4], bf16x8 f[8]) {
+    constexpr int RB = Tile<kBD>::ROW_BYTES;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const ATTN_LDS char* a = tile + ofs[t] + 16 * u * RB;
+            const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)a);
+            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)(a + 8 * RB));
+            f[4 * u + t] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+}
+__device__ __forceinline__ void tr_products(const bf16x8 f[8], const bf16x8 pk[2], f32x16 acc[4]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = mfma_bf16(f[4 * u + t], pk[u], acc[t]);
+}
+
 // Writes acc (C layout: rows = d, column = lane's row r0 + l32) scaled by f as
 // bf16 rows of [N][128].
 __device__ __forceinline__ void store_rows(__bf16* head, int r0, int N, int lane, const f32x16 acc[4], float f) {
@@ -342,6 +364,10 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int bid, BwdLds& sm
         for (int st = 0; st < 8; ++st) s = mfma_bf16(kr[st], qf[st], s);
 #pragma unroll
         for (int st = 0; st < 8; ++st) dp = mfma_bf16(vr[st], df[st], dp);
+        // K^T fragments of the dQ products, read while the probabilities are computed
+        bf16x8 ktf[8];
+        tr_frags((const ATTN_LDS char*)lds[buf][0], ofs, ktf);
+        asm volatile("" ::: "memory");
         bf16x8 sk[2];
         auto probs = [&](auto mask_c) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_c)::value;
@@ -355,7 +381,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int bid, BwdLds& sm
         };
         if (full) probs(std::integral_constant<bool, false>{});
         else probs(std::integral_constant<bool, true>{});
-        tr_gemm((const ATTN_LDS char*)lds[buf][0], ofs, sk, dq);   // dQ^T += K^T dS^T
+        tr_products(ktf, sk, dq);   // dQ^T += K^T dS^T
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next barrier
     };
     if (nkc > 0) issue(0, 0);
