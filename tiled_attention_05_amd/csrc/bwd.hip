@@ -288,8 +288,13 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid, BwdLds& 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * r4 + e, qrow = i0 + q4 + e;
-                const bool ok = qrow < p.N && key < p.N && (!p.causal || key <= qrow);
-                const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - l4[e] * kLog2e) : 0.f;
+                // branch-free: the exponential of every element, then a select
+                // (a short-circuit condition around it became per-element
+                // exec-mask branches); keys and queries past N are clamped rows,
+                // so the discarded values are finite or +inf, never read
+                const bool ok = (qrow < p.N) & (key < p.N) & (!p.causal | (key <= qrow));
+                const float ex = fast_exp2(s[r] * p.scale_log2 - l4[e] * kLog2e);
+                const float pr = ok ? ex : 0.f;
                 pk[r >> 3][r & 7] = (__bf16)pr;
                 sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - d4[e]));
             }
@@ -374,8 +379,9 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int bid, BwdLds& sm
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool ok = !MASK || (qrow < p.N && key < p.N && (!p.causal || key <= qrow));
-                const float pr = ok ? fast_exp2(s[r] * p.scale_log2 - lse2) : 0.f;
+                const bool ok = !MASK || ((qrow < p.N) & (key < p.N) & (!p.causal | (key <= qrow)));
+                const float ex = fast_exp2(s[r] * p.scale_log2 - lse2);   // branch-free, as in dK / dV
+                const float pr = ok ? ex : 0.f;
                 sk[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dd));
             }
         };
