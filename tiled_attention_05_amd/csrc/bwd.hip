@@ -280,6 +280,12 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid, BwdLds& 
             dp = mfma_bf16(af[st], vf, dp);
         }
         bf16x8 pk[2], sk[2];
+        // Element r of the lane is query i0 + 4 hh + c, c = 8 (r / 4) + r % 4:
+        // allowed when lo <= c < lo + range (one unsigned compare per element;
+        // range 0 when the lane's key is past N)
+        const int base = i0 + 4 * hh;
+        const int lo = p.causal ? key - base : -kBC;
+        const int range = key < p.N ? max(p.N - base - lo, 0) : 0;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int q4 = 8 * r4 + 4 * hh;   // queries q4 .. q4 + 3 of the chunk
@@ -287,12 +293,12 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, int bid, BwdLds& 
             const f32x4 d4 = *(const ATTN_LDS f32x4*)((const ATTN_LDS float*)stat[buf] + kBC + q4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 4 * r4 + e, qrow = i0 + q4 + e;
+                const int r = 4 * r4 + e;
                 // branch-free: the exponential of every element, then a select
                 // (a short-circuit condition around it became per-element
                 // exec-mask branches); keys and queries past N are clamped rows,
                 // so the discarded values are finite or +inf, never read
-                const bool ok = (qrow < p.N) & (key < p.N) & (!p.causal | (key <= qrow));
+                const bool ok = (unsigned)(8 * r4 + e - lo) < (unsigned)range;
                 const float ex = fast_exp2(s[r] * p.scale_log2 - l4[e] * kLog2e);
                 const float pr = ok ? ex : 0.f;
                 pk[r >> 3][r & 7] = (__bf16)pr;
