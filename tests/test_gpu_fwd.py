@@ -292,15 +292,18 @@ torch.save([(o.cpu(), l.cpu()) for o, l in outs], sys.argv[2])
 
 def persistent_cases():
     """Outputs of a few launches (causal, GQA + window, documents + mods, varlen).
-    The last three have more work items than an MI355X has CUs (512, 512 and
-    over 300 list entries per head), so each persistent workgroup runs several
-    items and reuses its LDS buffers (output staging included) from one item to
-    the next."""
+    The last five have more work items than an MI355X has CUs (384 to 1024
+    items, and over 300 list entries per head), so each persistent workgroup
+    runs several items and reuses its LDS buffers (output staging included)
+    from one item to the next (row counts not a multiple of the 256-row tile
+    included)."""
     outs = []
     for w, docs in ((I.WORKLOADS[2].shrink(B=2, Hq=8, Hkv=8, N=1000), None),
                     (I.WORKLOADS[3].shrink(B=1, Hq=16, Hkv=4, N=1500, window=300), None),
                     (I.WORKLOADS[4].shrink(B=1, Hq=4, Hkv=4, N=2500), (64, 1024)),
                     (I.WORKLOADS[2].shrink(B=2, Hq=16, Hkv=16, N=4096), None),
+                    (I.WORKLOADS[2].shrink(B=4, Hq=32, Hkv=32, N=2000), None),
+                    (I.WORKLOADS[3].shrink(B=1, Hq=32, Hkv=8, N=3000, window=700), None),
                     (I.WORKLOADS[4].shrink(B=1, Hq=16, Hkv=16, N=8192), (64, 2048))):
         outs.append(run_fwd(_case(w, doc_range=docs), w.mask, w.window, w.softcap))
     lengths = [5000, 1, 777, 3000, 20000, 129, 9000, 2000, 300, 24590]   # 64 K tokens
