@@ -35,7 +35,10 @@
 // (FR)", section "Architecture technique", item 1). The running max used as
 // the exponent reference is only moved when the row max has grown by more than
 // 2^8 ("lazy" rescale): the output accumulator is then rescaled rarely, and the
-// result is unchanged because O / l and the LSE use the same reference.
+// result is unchanged because O / l and the LSE use the same reference. On full
+// tiles without modifiers the exponents are first taken against the current
+// reference; the row max is computed only when some lane's partial sum of p
+// (a bound on each of its p) shows that a reference may have to move.
 // Masked tiles and score modifiers first rewrite the scores in place (exp2
 // units, -inf where not allowed); the softmax code is then the same.
 //
@@ -99,6 +102,9 @@ namespace attn {
 
 constexpr float kLazyTau = 8.f;     // log2 units: rescale O only when the max grows by > 2^8
 constexpr float kNoMax = -1e30f;    // initial reference: finite, below any score
+// A lane's partial row sum of p bounds each of its p; at or below this limit
+// every p is below 2^(kLazyTau - 0.005), i.e. no reference moves.
+constexpr float kSpecSumLimit = 255.f;
 
 // LDS of one workgroup of the bf16 forward.
 template <int D, bool DOC>
@@ -506,42 +512,6 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
     auto softmax = [&](int kt, const ATTN_LDS int* dl) __attribute__((always_inline)) {
         const bool full = is_full(kt, dl);
         const bool pre = MODS || !full || !(c > 0.f);
-        // lane part of the ALiBi bias (see prepare_scores), 0 without ALiBi
-        const float alibi_lane = ALIBI ? slope_l2 * (float)(kt * BN + 4 * hh - row) : 0.f;
-        // With score modifiers, once every row of the wave has a reference the
-        // scores are prepared relative to it (the modifier's last FMA adds
-        // alibi_lane - m), so that the exponent needs no argument instruction
-        // on tiles where no row's reference moves.
-        const bool rel = MODS && __builtin_amdgcn_ballot_w64(!(m > kNoMax)) == 0;
-        if (pre) prepare_scores(full, kt, dl, rel ? alibi_lane - m : 0.f);
-        const float ce = pre ? 1.f : c;
-        float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) {
-            a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
-            a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
-        }
-        a0 = max3(a0, sacc[0][15], max2(a1, sacc[1][15]));
-        bool need;
-        float alpha, ce2, mneg;   // p = exp2(s ce2 + mneg)
-        if (rel) {
-            const float mx = xhalf_max(a0);   // the tile's max over the reference
-            need = mx > kLazyTau;
-            alpha = need ? fast_exp2(-mx) : 1.f;
-            m = need ? m + mx : m;
-            ce2 = 1.f;
-            mneg = need ? -mx : 0.f;
-        } else {
-            const float mx = xhalf_max(a0 + alibi_lane) * ce;
-            const float mn = max2(m, mx);
-            need = mn > m + kLazyTau;
-            alpha = need ? fast_exp2(m - mn) : 1.f;
-            m = need ? mn : m;
-            ce2 = ce;
-            mneg = alibi_lane - m;
-        }
-        // relative scores and no reference moved: the exponent of the score itself
-        const bool plain = rel && __builtin_amdgcn_ballot_w64(need) == 0;
         float ls0 = -0.f, ls1 = -0.f, ls2 = -0.f, ls3 = -0.f;   // -0 + p folds to p
         auto exps = [&](auto arg) __attribute__((always_inline)) {
 #pragma unroll
@@ -555,10 +525,69 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                     pf[kb][r >> 3][(r & 7) + 1] = (__bf16)p1;
                 }
         };
-        if (plain)
-            exps([](float x) __attribute__((always_inline)) { return x; });
-        else
-            exps([&](float x) __attribute__((always_inline)) { return __builtin_fmaf(x, ce2, mneg); });
+        bool need = false;
+        float alpha = 1.f;
+        // The pass with the tile's row max: references moved where it grew by
+        // more than 2^kLazyTau, then the exponents (prepared scores when the
+        // tile needed modifiers or the element mask, else raw ones).
+        auto max_pass = [&](auto prepared_c) __attribute__((always_inline)) {
+            constexpr bool PREP = decltype(prepared_c)::value;
+            // lane part of the ALiBi bias (see prepare_scores), 0 without ALiBi
+            const float alibi_lane = ALIBI ? slope_l2 * (float)(kt * BN + 4 * hh - row) : 0.f;
+            // With score modifiers, once every row of the wave has a reference the
+            // scores are prepared relative to it (the modifier's last FMA adds
+            // alibi_lane - m), so that the exponent needs no argument instruction
+            // on tiles where no row's reference moves.
+            const bool rel = MODS && __builtin_amdgcn_ballot_w64(!(m > kNoMax)) == 0;
+            if (PREP) prepare_scores(full, kt, dl, rel ? alibi_lane - m : 0.f);
+            const float ce = PREP ? 1.f : c;
+            float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
+#pragma unroll
+            for (int r = 3; r < 15; r += 2) {
+                a0 = max3(a0, sacc[0][r], sacc[0][r + 1]);
+                a1 = max3(a1, sacc[1][r], sacc[1][r + 1]);
+            }
+            a0 = max3(a0, sacc[0][15], max2(a1, sacc[1][15]));
+            float ce2, mneg;   // p = exp2(s ce2 + mneg)
+            if (rel) {
+                const float mx = xhalf_max(a0);   // the tile's max over the reference
+                need = mx > kLazyTau;
+                alpha = need ? fast_exp2(-mx) : 1.f;
+                m = need ? m + mx : m;
+                ce2 = 1.f;
+                mneg = need ? -mx : 0.f;
+            } else {
+                const float mx = xhalf_max(a0 + alibi_lane) * ce;
+                const float mn = max2(m, mx);
+                need = mn > m + kLazyTau;
+                alpha = need ? fast_exp2(m - mn) : 1.f;
+                m = need ? mn : m;
+                ce2 = ce;
+                mneg = alibi_lane - m;
+            }
+            // relative scores and no reference moved: the exponent of the score itself
+            const bool plain = rel && __builtin_amdgcn_ballot_w64(need) == 0;
+            if (plain)
+                exps([](float x) __attribute__((always_inline)) { return x; });
+            else
+                exps([&](float x) __attribute__((always_inline)) { return __builtin_fmaf(x, ce2, mneg); });
+        };
+        if (pre) {
+            max_pass(std::integral_constant<bool, true>{});
+        } else {
+            // Full tiles without modifiers: the exponents against the current
+            // references first. When no lane's partial sum exceeds
+            // kSpecSumLimit no row's reference would move, and these are the
+            // values the max pass gives, without that pass; otherwise (the
+            // first tile of a row too, its reference still kNoMax) the max
+            // pass recomputes the tile.
+            const float mneg = -m;
+            exps([&](float x) __attribute__((always_inline)) { return __builtin_fmaf(x, c, mneg); });
+            if (__builtin_amdgcn_ballot_w64(!((ls0 + ls1) + (ls2 + ls3) <= kSpecSumLimit)) != 0) {
+                ls0 = ls1 = ls2 = ls3 = -0.f;
+                max_pass(std::integral_constant<bool, false>{});
+            }
+        }
         // P is complete here; GEMM1 reads it only after the wait states below
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
