@@ -35,10 +35,10 @@
 // (FR)", section "Architecture technique", item 1). The running max used as
 // the exponent reference is only moved when the row max has grown by more than
 // 2^8 ("lazy" rescale): the output accumulator is then rescaled rarely, and the
-// result is unchanged because O / l and the LSE use the same reference. On full
-// tiles without modifiers the exponents are first taken against the current
-// reference; the row max is computed only when some lane's partial sum of p
-// (a bound on each of its p) shows that a reference may have to move.
+// result is unchanged because O / l and the LSE use the same reference. The
+// exponents are first taken against the current references; the row max is
+// computed only when some lane's partial sum of p (a bound on each of its p)
+// shows that a reference may have to move.
 // Masked tiles and score modifiers first rewrite the scores in place (exp2
 // units, -inf where not allowed); the softmax code is then the same.
 //
@@ -525,22 +525,30 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                     pf[kb][r >> 3][(r & 7) + 1] = (__bf16)p1;
                 }
         };
+        // lane part of the ALiBi bias (see prepare_scores), 0 without ALiBi
+        const float alibi_lane = ALIBI ? slope_l2 * (float)(kt * BN + 4 * hh - row) : 0.f;
+        // With score modifiers, once every row of the wave has a reference the
+        // scores are prepared relative to it (the modifier's last FMA adds
+        // alibi_lane - m), so that the exponent needs no argument instruction
+        // on tiles where no row's reference moves.
+        const bool rel = MODS && __builtin_amdgcn_ballot_w64(!(m > kNoMax)) == 0;
+        if (__builtin_expect(pre, MODS)) prepare_scores(full, kt, dl, rel ? alibi_lane - m : 0.f);
+        const float ce = pre ? 1.f : c;
+        // The exponents against the current references first. When no lane's
+        // partial sum exceeds kSpecSumLimit, no row's reference would move and
+        // these are the values the pass with the tile's row max gives, without
+        // that pass; otherwise (the first tile of a row too, its reference
+        // still kNoMax) that pass recomputes the tile.
+        if (rel) {
+            exps([](float x) __attribute__((always_inline)) { return x; });
+        } else {
+            const float mneg0 = alibi_lane - m;
+            exps([&](float x) __attribute__((always_inline)) { return __builtin_fmaf(x, ce, mneg0); });
+        }
         bool need = false;
         float alpha = 1.f;
-        // The pass with the tile's row max: references moved where it grew by
-        // more than 2^kLazyTau, then the exponents (prepared scores when the
-        // tile needed modifiers or the element mask, else raw ones).
-        auto max_pass = [&](auto prepared_c) __attribute__((always_inline)) {
-            constexpr bool PREP = decltype(prepared_c)::value;
-            // lane part of the ALiBi bias (see prepare_scores), 0 without ALiBi
-            const float alibi_lane = ALIBI ? slope_l2 * (float)(kt * BN + 4 * hh - row) : 0.f;
-            // With score modifiers, once every row of the wave has a reference the
-            // scores are prepared relative to it (the modifier's last FMA adds
-            // alibi_lane - m), so that the exponent needs no argument instruction
-            // on tiles where no row's reference moves.
-            const bool rel = MODS && __builtin_amdgcn_ballot_w64(!(m > kNoMax)) == 0;
-            if (PREP) prepare_scores(full, kt, dl, rel ? alibi_lane - m : 0.f);
-            const float ce = PREP ? 1.f : c;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!((ls0 + ls1) + (ls2 + ls3) <= kSpecSumLimit)) != 0, 0)) {
+            ls0 = ls1 = ls2 = ls3 = -0.f;
             float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
 #pragma unroll
             for (int r = 3; r < 15; r += 2) {
@@ -571,22 +579,6 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
                 exps([](float x) __attribute__((always_inline)) { return x; });
             else
                 exps([&](float x) __attribute__((always_inline)) { return __builtin_fmaf(x, ce2, mneg); });
-        };
-        if (pre) {
-            max_pass(std::integral_constant<bool, true>{});
-        } else {
-            // Full tiles without modifiers: the exponents against the current
-            // references first. When no lane's partial sum exceeds
-            // kSpecSumLimit no row's reference would move, and these are the
-            // values the max pass gives, without that pass; otherwise (the
-            // first tile of a row too, its reference still kNoMax) the max
-            // pass recomputes the tile.
-            const float mneg = -m;
-            exps([&](float x) __attribute__((always_inline)) { return __builtin_fmaf(x, c, mneg); });
-            if (__builtin_amdgcn_ballot_w64(!((ls0 + ls1) + (ls2 + ls3) <= kSpecSumLimit)) != 0) {
-                ls0 = ls1 = ls2 = ls3 = -0.f;
-                max_pass(std::integral_constant<bool, false>{});
-            }
         }
         // P is complete here; GEMM1 reads it only after the wait states below
 #pragma unroll
