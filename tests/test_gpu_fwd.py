@@ -160,6 +160,22 @@ def test_full_workload_whole_heads(k):
 
 
 # ------------------------------------------------------------------ determinism, capture, canaries
+@pytest.mark.parametrize("growth", [5.0, 40.0])
+@pytest.mark.parametrize("mask", [I.MASK_NONE, I.MASK_CAUSAL])
+def test_scores_growing_along_keys(growth, mask):
+    """Scores that grow along the keys (a ramp of `growth` log2 units over the
+    sequence, through one channel), so that later key tiles exceed each row's
+    exponent reference: by a few units (the exponents recomputed after the
+    tile's row max, no reference moved) or by many (references moved and the
+    output rescaled several times per row)."""
+    w = I.WORKLOADS[2].shrink(B=1, Hq=4, Hkv=4, N=1500, mask=mask)
+    x = I.inputs(w, seed=5)
+    ramp = growth * torch.arange(w.N, dtype=torch.float64) / (w.N - 1) / (w.scale * math.log2(math.e))
+    x["q"][..., 0] = 1.0
+    x["k"][..., 0] = ramp.to(torch.bfloat16)
+    _check(w, x, f"scores growing by {growth} log2 units along the keys, mask {mask}")
+
+
 def test_bitwise_deterministic():
     w = I.WORKLOADS[2].shrink(B=2, Hq=4, Hkv=4, N=1100)
     x = I.inputs(w)
