@@ -37,8 +37,8 @@
 // 2^8 ("lazy" rescale): the output accumulator is then rescaled rarely, and the
 // result is unchanged because O / l and the LSE use the same reference. The
 // exponents are first taken against the current references; the row max is
-// computed only when some lane's partial sum of p (a bound on each of its p)
-// shows that a reference may have to move.
+// computed only when one of a lane's partial sums of p (a bound on each p in
+// it) shows that a reference may have to move.
 // Masked tiles and score modifiers first rewrite the scores in place (exp2
 // units, -inf where not allowed); the softmax code is then the same.
 //
@@ -102,8 +102,8 @@ namespace attn {
 
 constexpr float kLazyTau = 8.f;     // log2 units: rescale O only when the max grows by > 2^8
 constexpr float kNoMax = -1e30f;    // initial reference: finite, below any score
-// A lane's partial row sum of p bounds each of its p; at or below this limit
-// every p is below 2^(kLazyTau - 0.005), i.e. no reference moves.
+// Each of a lane's partial sums of p (8 p each) bounds the p it holds; at or
+// below this limit every p is below 2^(kLazyTau - 0.005): no reference moves.
 constexpr float kSpecSumLimit = 255.f;
 
 // LDS of one workgroup of the bf16 forward.
@@ -534,8 +534,8 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
         const bool rel = MODS && __builtin_amdgcn_ballot_w64(!(m > kNoMax)) == 0;
         if (__builtin_expect(pre, MODS)) prepare_scores(full, kt, dl, rel ? alibi_lane - m : 0.f);
         const float ce = pre ? 1.f : c;
-        // The exponents against the current references first. When no lane's
-        // partial sum exceeds kSpecSumLimit, no row's reference would move and
+        // The exponents against the current references first. When no partial
+        // sum of p exceeds kSpecSumLimit, no row's reference would move and
         // these are the values the pass with the tile's row max gives, without
         // that pass; otherwise (the first tile of a row too, its reference
         // still kNoMax) that pass recomputes the tile.
@@ -547,7 +547,7 @@ __device__ __attribute__((always_inline)) void fwd_bf16_item(const FwdParams& p,
         }
         bool need = false;
         float alpha = 1.f;
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!((ls0 + ls1) + (ls2 + ls3) <= kSpecSumLimit)) != 0, 0)) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(max2(max3(ls0, ls1, ls2), ls3) <= kSpecSumLimit)) != 0, 0)) {
             ls0 = ls1 = ls2 = ls3 = -0.f;
             float a0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]), a1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
 #pragma unroll
